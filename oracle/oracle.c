@@ -1,0 +1,279 @@
+/*
+ * CPU ORACLE for MoE token dispatch / combine -- TEST INFRASTRUCTURE ONLY.
+ *
+ * Plain, slow, single-threaded C.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this file's library.  It shares no code
+ * with the HIP implementation and never calls it.
+ *
+ * Source of the definitions: "NJU x Huawei UBEP: Reengineering MoE Expert
+ * Parallelism" (kad8.com).
+ *   - opening section: every token is sent to the device hosting each expert it
+ *     selected, and the results are gathered back to the token in the Combine
+ *     phase (dispatch / combine);
+ *   - "BSP Serialization": the dispatch pipeline is send tokens, send token
+ *     counts, calculate offsets, reorder tokens;
+ *   - "Kernel Decomposition": metadata work is token counting, prefix sums and
+ *     offset calculation.
+ * The pages give no formula for any of these.  The readings taken here:
+ *   - expert e lives on rank floor(e / (E/R)); token t belongs to source rank
+ *     floor(t / (T/R)) and to chunk floor(t / (T/C));
+ *   - one receive row per (token, slot) pair, no de-duplication;
+ *   - a rank's receive region holds its rows in (token, slot) order and the
+ *     regions are packed back to back in rank order;
+ *   - combine is an fp32 fused-multiply-add chain over slots 0..k-1 starting
+ *     from +0.0f, rounded once to bf16 (round to nearest, ties to even);
+ *   - fp8 payload: per token and per block of 128 channels, scale
+ *     s = amax / 448 (IEEE fp32 division; s = 1 when amax = 0) and code
+ *     q = E4M3(x / s), rounded to nearest with ties to even and saturated at
+ *     +-448 (OCP 8-bit floating point, E4M3 "FN" flavour: bias 7, no infinity).
+ * Every function here computes exactly that definition with plain loops.
+ *
+ * Parity status: every function is pinned by the CPU tests (library special
+ * cases, brute force on tiny inputs, exact rational arithmetic, closed forms).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "oracle.h"
+
+/* ------------------------------------------------------------------------ */
+/* shape rules that the definition itself needs                             */
+/* ------------------------------------------------------------------------ */
+int oracle_check_shape(int64_t T, int64_t H, int32_t E, int32_t k, int32_t R, int32_t C,
+                       int fp8)
+{
+    if (T <= 0 || H <= 0 || E <= 0 || k <= 0 || R <= 0 || C <= 0) return ORACLE_INVALID_ARG;
+    if (k > E) return ORACLE_INVALID_ARG;            /* k distinct experts per token */
+    if (E % R != 0) return ORACLE_INVALID_ARG;       /* equal expert blocks per rank  */
+    if (T % R != 0) return ORACLE_INVALID_ARG;       /* equal token blocks per source */
+    if (T % C != 0) return ORACLE_INVALID_ARG;       /* equal token blocks per chunk  */
+    if (fp8 && H % 128 != 0) return ORACLE_INVALID_ARG; /* whole 128-channel blocks */
+    if (T * (int64_t)k >= ((int64_t)1 << 30)) return ORACLE_INVALID_ARG;
+    return ORACLE_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* layout: counts -> exclusive prefix sums -> stable positions              */
+/* ------------------------------------------------------------------------ */
+int oracle_layout(int64_t T, int32_t E, int32_t k, int32_t R, int32_t C,
+                  const int32_t *topk_idx,
+                  int32_t *pos, int32_t *expert_count, int32_t *rank_count,
+                  int32_t *recv_offset, int32_t *send_offset, int32_t *chunk_offset,
+                  int32_t *recv_src)
+{
+    int st = oracle_check_shape(T, 8, E, k, R, C, 0);
+    if (st != ORACLE_OK) return st;
+    for (int64_t i = 0; i < T * k; ++i)
+        if (topk_idx[i] < 0 || topk_idx[i] >= E) return ORACLE_BAD_EXPERT_ID;
+
+    const int32_t epr = E / R;          /* experts per rank  */
+    const int64_t tps = T / R;          /* tokens per source */
+    const int64_t tpc = T / C;          /* tokens per chunk  */
+
+    int32_t *sd_count = calloc((size_t)R * R, sizeof(int32_t));
+    int32_t *cd_count = calloc((size_t)C * R, sizeof(int32_t));
+    int32_t *cursor = calloc((size_t)R, sizeof(int32_t));
+    if (!sd_count || !cd_count || !cursor) {
+        free(sd_count); free(cd_count); free(cursor);
+        return ORACLE_UNSUPPORTED;
+    }
+
+    /* 1. token counts */
+    for (int32_t e = 0; e < E; ++e) expert_count[e] = 0;
+    for (int32_t d = 0; d < R; ++d) rank_count[d] = 0;
+    for (int64_t t = 0; t < T; ++t) {
+        for (int32_t j = 0; j < k; ++j) {
+            int32_t e = topk_idx[t * k + j];
+            int32_t d = e / epr;
+            int64_t s = t / tps;
+            int64_t c = t / tpc;
+            expert_count[e] += 1;
+            rank_count[d] += 1;
+            sd_count[s * R + d] += 1;
+            cd_count[c * R + d] += 1;
+        }
+    }
+
+    /* 2. exclusive prefix sums */
+    recv_offset[0] = 0;
+    for (int32_t d = 0; d < R; ++d) recv_offset[d + 1] = recv_offset[d] + rank_count[d];
+    for (int32_t d = 0; d < R; ++d) {
+        int32_t run = 0;
+        for (int32_t s = 0; s < R; ++s) {
+            send_offset[s * R + d] = run;
+            run += sd_count[s * R + d];
+        }
+    }
+    if (chunk_offset) {
+        for (int32_t d = 0; d < R; ++d) {
+            int32_t run = 0;
+            for (int32_t c = 0; c < C; ++c) {
+                chunk_offset[c * R + d] = run;
+                run += cd_count[c * R + d];
+            }
+        }
+    }
+
+    /* 3. stable positions: rows in (destination rank, token, slot) order */
+    for (int32_t d = 0; d < R; ++d) cursor[d] = recv_offset[d];
+    for (int64_t t = 0; t < T; ++t) {
+        for (int32_t j = 0; j < k; ++j) {
+            int32_t d = topk_idx[t * k + j] / epr;
+            int32_t p = cursor[d]++;
+            pos[t * k + j] = p;
+            if (recv_src) recv_src[p] = (int32_t)(t * k + j);
+        }
+    }
+
+    free(sd_count); free(cd_count); free(cursor);
+    return ORACLE_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* number formats                                                           */
+/* ------------------------------------------------------------------------ */
+static float f32_from_bits(uint32_t u) { float f; memcpy(&f, &u, 4); return f; }
+static uint32_t bits_from_f32(float f) { uint32_t u; memcpy(&u, &f, 4); return u; }
+
+float oracle_bf16_to_f32(uint16_t b) { return f32_from_bits((uint32_t)b << 16); }
+
+/* Nearest bf16, ties to the even one.  bf16 keeps the top 16 bits of fp32;
+ * `lo` drops the low 16 bits (toward zero), `hi` is the next bf16 away from
+ * zero.  Compare the dropped half against one half unit. */
+uint16_t oracle_f32_to_bf16(float f)
+{
+    uint32_t u = bits_from_f32(f);
+    if (isnan(f)) return (uint16_t)((u >> 16) | 0x0040u);   /* quiet NaN */
+    uint32_t lo = u >> 16;
+    uint32_t hi = lo + 1u;
+    uint32_t rest = u & 0xFFFFu;
+    if (rest < 0x8000u) return (uint16_t)lo;
+    if (rest > 0x8000u) return (uint16_t)hi;
+    return (uint16_t)((lo & 1u) ? hi : lo);
+}
+
+/* Closed-form E4M3FN value of a code: sign S, exponent field X (4 bits, bias 7),
+ * mantissa M (3 bits).  X = 0 is subnormal 2^-6 * M/8; X = 15, M = 7 is NaN. */
+float oracle_e4m3_to_f32(uint8_t c)
+{
+    int S = c >> 7, X = (c >> 3) & 15, M = c & 7;
+    double v;
+    if (X == 15 && M == 7) return NAN;
+    if (X == 0) v = ldexp((double)M / 8.0, -6);
+    else v = ldexp(1.0 + (double)M / 8.0, X - 7);
+    return (float)(S ? -v : v);
+}
+
+/* Values of the 127 non-negative finite codes 0x00..0x7E, in increasing order. */
+static double e4m3_value[127];
+static int e4m3_value_ready = 0;
+
+static void e4m3_build_values(void)
+{
+    for (int c = 0; c < 127; ++c) e4m3_value[c] = (double)oracle_e4m3_to_f32((uint8_t)c);
+    e4m3_value_ready = 1;
+}
+
+/* Nearest E4M3FN code, ties to the even code, magnitudes beyond 448 saturate
+ * to 448.  Binary-search the value table for the largest code not above |f|,
+ * then compare the distances to it and to the next code; in double these
+ * distances are exact for fp32 operands below 448. */
+uint8_t oracle_f32_to_e4m3(float f)
+{
+    if (!e4m3_value_ready) e4m3_build_values();
+    if (isnan(f)) return 0x7F;
+    uint8_t sign = signbit(f) ? 0x80 : 0x00;
+    double a = fabs((double)f);
+    if (a >= 448.0) return (uint8_t)(sign | 0x7E);
+    int lo = 0, hi = 126;                       /* e4m3_value[lo] <= a < e4m3_value[hi] */
+    while (hi - lo > 1) {
+        int mid = (lo + hi) / 2;
+        if (e4m3_value[mid] <= a) lo = mid; else hi = mid;
+    }
+    double dlo = a - e4m3_value[lo], dhi = e4m3_value[hi] - a;
+    int pick;
+    if (dlo < dhi) pick = lo;
+    else if (dhi < dlo) pick = hi;
+    else pick = (lo & 1) ? hi : lo;
+    return (uint8_t)(sign | pick);
+}
+
+/* ------------------------------------------------------------------------ */
+/* dispatch                                                                 */
+/* ------------------------------------------------------------------------ */
+void oracle_dispatch_bf16(int64_t T, int64_t H, int32_t k, const uint16_t *x,
+                          const int32_t *pos, uint16_t *recv)
+{
+    for (int64_t t = 0; t < T; ++t)
+        for (int32_t j = 0; j < k; ++j)
+            memcpy(recv + (int64_t)pos[t * k + j] * H, x + t * H, (size_t)H * sizeof(uint16_t));
+}
+
+void oracle_dispatch_fp8(int64_t T, int64_t H, int32_t k, const uint16_t *x,
+                         const int32_t *pos, uint8_t *recv8, float *recv_scale)
+{
+    const int64_t nb = H / 128;
+    uint8_t q[128];
+    for (int64_t t = 0; t < T; ++t) {
+        for (int64_t b = 0; b < nb; ++b) {
+            const uint16_t *xb = x + t * H + b * 128;
+            float amax = 0.0f;
+            for (int c = 0; c < 128; ++c) {
+                float v = fabsf(oracle_bf16_to_f32(xb[c]));
+                if (v > amax) amax = v;
+            }
+            float s = amax > 0.0f ? amax / 448.0f : 1.0f;
+            for (int c = 0; c < 128; ++c) q[c] = oracle_f32_to_e4m3(oracle_bf16_to_f32(xb[c]) / s);
+            for (int32_t j = 0; j < k; ++j) {
+                int64_t p = pos[t * k + j];
+                memcpy(recv8 + p * H + b * 128, q, 128);
+                recv_scale[p * nb + b] = s;
+            }
+        }
+    }
+}
+
+/* identity expert for an fp8 payload: y = bf16(decode(q) * s), one fp32 multiply */
+void oracle_identity_fp8(int64_t rows, int64_t H, const uint8_t *q, const float *scale,
+                         uint16_t *y)
+{
+    const int64_t nb = H / 128;
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t c = 0; c < H; ++c)
+            y[r * H + c] = oracle_f32_to_bf16(oracle_e4m3_to_f32(q[r * H + c]) *
+                                              scale[r * nb + c / 128]);
+}
+
+/* ------------------------------------------------------------------------ */
+/* combine                                                                  */
+/* ------------------------------------------------------------------------ */
+void oracle_combine(int64_t T, int64_t H, int32_t k, const uint16_t *y, const int32_t *pos,
+                    const float *topk_w, uint16_t *out)
+{
+    for (int64_t t = 0; t < T; ++t) {
+        for (int64_t c = 0; c < H; ++c) {
+            float acc = 0.0f;
+            for (int32_t j = 0; j < k; ++j) {
+                float v = oracle_bf16_to_f32(y[(int64_t)pos[t * k + j] * H + c]);
+                acc = fmaf(topk_w[t * k + j], v, acc);
+            }
+            out[t * H + c] = oracle_f32_to_bf16(acc);
+        }
+    }
+}
+
+/* element-wise helpers exposed for the pins */
+void oracle_f32_to_e4m3_array(int64_t n, const float *in, uint8_t *out)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_f32_to_e4m3(in[i]);
+}
+void oracle_f32_to_bf16_array(int64_t n, const float *in, uint16_t *out)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_f32_to_bf16(in[i]);
+}
+void oracle_e4m3_to_f32_array(int64_t n, const uint8_t *in, float *out)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_e4m3_to_f32(in[i]);
+}
