@@ -1,0 +1,258 @@
+#!/usr/bin/env python3
+"""MoE token dispatch + combine on one MI355X: HBM GB/s and tokens/s.
+
+One step = the whole path over one synthetic batch already resident in HBM:
+ubep_layout (counts, prefix sums, positions) -> ubep_dispatch (rows into the
+R receive regions) -> identity expert (y = recv) -> ubep_combine (slot-ordered
+FMA chain back to token order).  `--mode chunked` runs layout + the one-kernel
+chunk pipeline instead of the two row kernels.
+
+Throughput counts algorithmic bytes (what the path must read and write):
+  layout   4Tk (ids) + 4Tk (positions)
+  dispatch 2TH + 4Tk + 2TkH            (bf16)   |  2TH + 4Tk + TkH + 4TkH/128  (fp8)
+  combine  2TkH + 8Tk + 2TH
+Time comes from HIP events on the stream the library launches on.
+
+Prints one JSON line.  Only one GPU is measured: `--gpus N` with N > 1 exits
+with a message.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "dispatch+combine HBM GB/s (% of MI355X peak) and tokens/s, 1 GPU"
+HBM_PEAK_GBS = 8000.0
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "hbm_counters.txt")
+
+
+def algorithmic_bytes(s: dict, fp8: bool) -> dict:
+    T, H, k = s["T"], s["H"], s["k"]
+    layout = 8 * T * k
+    if fp8:
+        dispatch = 2 * T * H + 4 * T * k + T * k * H + 4 * T * k * (H // 128)
+    else:
+        dispatch = 2 * T * H + 4 * T * k + 2 * T * k * H
+    combine = 2 * T * k * H + 8 * T * k + 2 * T * H
+    return dict(layout=layout, dispatch=dispatch, combine=combine,
+                total=layout + dispatch + combine)
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "combine_top_route_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_counters(kernel: str, workload: str):
+    """HBM traffic of `kernel` from the committed rocprofv3 counter summary,
+    scaled by the copy-kernel calibration; None when absent or when the
+    kernel sources changed after the counters were taken."""
+    if not os.path.exists(COUNTERS_FILE):
+        return None
+    rows = {}
+    with open(COUNTERS_FILE) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            kv = dict(p.split("=", 1) for p in line.split())
+            rows[(kv.get("kind"), kv.get("kernel"), kv.get("workload"))] = kv
+    cal = next((v for (kind, _, _), v in rows.items() if kind == "copy"), None)
+    got = rows.get(("kernel", kernel, workload))
+    if cal is None or got is None or got.get("source") != source_hash():
+        return None
+    copy_bytes = float(cal["bytes"])
+    f_scale = copy_bytes / (float(cal["fetch_kib"]) * 1024.0)
+    w_scale = copy_bytes / (float(cal["write_kib"]) * 1024.0)
+    return float(got["fetch_kib"]) * 1024.0 * f_scale + float(got["write_kib"]) * 1024.0 * w_scale
+
+
+def cpu_baseline(w, reps: int) -> dict:
+    """The CPU oracle (single-threaded C) on the same batch: layout + dispatch
+    + combine, outputs preallocated, median of `reps` runs."""
+    import numpy as np
+
+    import oracle
+    s = w.shape
+    fp8 = w.recipe.payload == "fp8"
+    rows = s.T * s.k
+    recv = np.empty((rows, s.H), np.uint16) if not fp8 else None
+    out = np.empty((s.T, s.H), np.uint16)
+    times = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        L = oracle.layout(w.topk_idx, s.E, s.R, s.C, want_src=False)
+        if fp8:
+            q, sc = oracle.dispatch_fp8(w.x, L["pos"])
+            t1 = time.perf_counter()
+            y = oracle.identity_fp8(q, sc)         # the identity expert is not timed
+            t2 = time.perf_counter()
+        else:
+            y = oracle.dispatch_bf16(w.x, L["pos"], recv=recv)
+            t1 = t2 = time.perf_counter()
+        oracle.combine(y, L["pos"], w.topk_w, out=out)
+        t3 = time.perf_counter()
+        times.append((t1 - t0) + (t3 - t2))
+    med = statistics.median(times)
+    nbytes = algorithmic_bytes(s.as_dict(), fp8)["total"]
+    return {"value": round(nbytes / med / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"whole batch ({s.T} tokens) of the benchmarked workload, "
+                      f"median of {reps} runs of layout+dispatch+combine, one thread",
+            "seconds_per_step": round(med, 4), "tokens_per_s": round(s.T / med, 1),
+            "host_cores_available": len(os.sched_getaffinity(0))}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=None, help="workload name (default: DeepSeek-V3 decode)")
+    ap.add_argument("--mode", choices=["unfused", "chunked"], default="unfused")
+    ap.add_argument("--cold", action="store_true",
+                    help="scrub the 256 MB memory-side cache between steps (outside the timing)")
+    ap.add_argument("--cpu-reps", type=int, default=7)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args(argv)
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the R expert-parallel ranks are regions of one "
+              "GPU's HBM and no multi-GPU path is built.", file=sys.stderr, flush=True)
+        return 2
+
+    import torch
+
+    import combine_top_route_amd as ubep
+    from combine_top_route_amd.buffers import alloc_buffers
+    from workloads import DEFAULT_BENCH, make_config
+
+    name = args.workload or DEFAULT_BENCH
+    w = make_config(name)
+    s = w.shape
+    sd = s.as_dict()
+    fp8 = w.recipe.payload == "fp8"
+    dtype = ubep.FP8_E4M3 if fp8 else ubep.BF16
+    if args.mode == "chunked" and fp8:
+        print("the chunk pipeline carries a bf16 payload only", file=sys.stderr)
+        return 2
+    torch.cuda.set_device(0)
+    b = alloc_buffers(sd, dtype, "cuda", x_bits=w.x, topk_idx=w.topk_idx, topk_w=w.topk_w)
+    stream = torch.cuda.current_stream()
+    chunk_off = b.chunk_offset if s.C > 1 else None
+    scrub = torch.empty(512 << 20, dtype=torch.uint8, device="cuda") if args.cold else None
+
+    def step(ev):
+        ev[0].record(stream)
+        ubep.ubep_layout(sd, b.topk_idx, b.pos, b.expert_count, b.rank_count, b.recv_offset,
+                         b.send_offset, chunk_off, None, b.ws, stream)
+        ev[1].record(stream)
+        if args.mode == "chunked":
+            ubep.ubep_dispatch_combine_chunked(sd, b.x, b.pos, b.topk_w, b.recv, b.out, None,
+                                               b.ws, stream=stream)
+            ev[2].record(stream)
+            ev[3].record(stream)
+            ev[4].record(stream)
+            return
+        ubep.ubep_dispatch(sd, dtype, b.x, b.pos, b.recv, b.recv_scale, b.ws, stream)
+        ev[2].record(stream)
+        if fp8:   # identity expert: between the timed calls, excluded from the step
+            ubep.ubep_identity_expert_fp8(s.T * s.k, s.H, b.recv, b.recv_scale, b.y, stream)
+        ev[3].record(stream)
+        ubep.ubep_combine(sd, b.y, b.pos, b.topk_w, b.out, b.ws, stream)
+        ev[4].record(stream)
+
+    def new_events():
+        return [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+
+    for _ in range(args.warmup):
+        step(new_events())
+    torch.cuda.synchronize()
+    st = ubep.ubep_get_device_status(b.ws)
+    if st != ubep.OK:
+        print(f"device status after warm-up: {ubep.STATUS_NAMES.get(st, st)}", file=sys.stderr)
+        return 1
+
+    evs = [new_events() for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    for i in range(args.steps):
+        if scrub is not None:
+            scrub.zero_()
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    st = ubep.ubep_get_device_status(b.ws)
+    if st != ubep.OK:
+        print(f"device status after timing: {ubep.STATUS_NAMES.get(st, st)}", file=sys.stderr)
+        return 1
+
+    lay = [e[0].elapsed_time(e[1]) for e in evs]
+    dis = [e[1].elapsed_time(e[2]) for e in evs]
+    com = [e[3].elapsed_time(e[4]) for e in evs]
+    step_ms = [a + d + c for a, d, c in zip(lay, dis, com)]
+    ms = statistics.fmean(step_ms)
+    nb = algorithmic_bytes(sd, fp8)
+    gbs = nb["total"] / (ms * 1e-3) / 1e9
+
+    if args.mode == "chunked":
+        dom, dom_ms, dom_bytes = "chunked", statistics.fmean(dis), nb["dispatch"] + nb["combine"]
+    elif statistics.fmean(dis) >= statistics.fmean(com):
+        dom, dom_ms, dom_bytes = "dispatch", statistics.fmean(dis), nb["dispatch"]
+    else:
+        dom, dom_ms, dom_bytes = "combine", statistics.fmean(com), nb["combine"]
+    achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
+    traffic = read_counters(dom, name)
+
+    rc = b.rank_count.cpu().numpy()
+    line = {
+        "metric": METRIC,
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3+bf16" if fp8 else "bf16",
+        "data": "synthetic",
+        "config": {"workload": name, **sd, "payload": w.recipe.payload, "mode": args.mode,
+                   "caches": "scrubbed between steps" if args.cold else "back-to-back steps",
+                   "seed": w.recipe.seed},
+        "pct_of_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
+        "tokens_per_s": round(s.T / (ms * 1e-3), 1),
+        "bytes_per_step": nb["total"],
+        "ms": {"layout": round(statistics.fmean(lay), 5), "dispatch": round(statistics.fmean(dis), 5),
+               "combine": round(statistics.fmean(com), 5),
+               "step_median": round(statistics.median(step_ms), 5)},
+        "wall_ms_per_step": round(1e3 * wall / args.steps, 5),
+        "rank_skew_max_over_mean": round(float(rc.max() / rc.mean()), 3),
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 2),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None if traffic is None else int(traffic),
+                     "algorithmic_bytes": dom_bytes},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, args.cpu_reps)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

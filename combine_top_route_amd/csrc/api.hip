@@ -1,0 +1,253 @@
+// C ABI (include/ubep.h): host-side validation, launch planning and status
+// handling.  Every argument check happens before anything is enqueued.
+#include <stdint.h>
+
+#include "launch.h"
+#include "ubep.h"
+
+namespace ubep {
+
+static int bits_for(int64_t n) {   // bits needed to hold the values 0..n-1
+    int b = 0;
+    while (((int64_t)1 << b) < n) ++b;
+    return b;
+}
+
+static int64_t gcd64(int64_t a, int64_t b) {
+    while (b != 0) {
+        const int64_t t = a % b;
+        a = b;
+        b = t;
+    }
+    return a;
+}
+
+static size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// A layout tile holds whole tokens and never straddles a source-rank or chunk
+// boundary: its token count divides gcd(T/R, T/C).  Take the largest such
+// divisor with at most kTileRowsMax rows.
+void make_plan(const ubep_shape& s, Plan* p) {
+    p->T = s.T;
+    p->H = s.H;
+    p->E = s.E;
+    p->k = s.k;
+    p->R = s.R;
+    p->C = s.C;
+    p->rows = s.T * s.k;
+    p->epr = s.E / s.R;
+    p->tps = s.T / s.R;
+    p->tpc = s.T / s.C;
+    const int64_t g = gcd64(p->tps, p->tpc);
+    int64_t cap = kTileRowsMax / s.k;
+    if (cap < 1) cap = 1;
+    int64_t tt = 1;
+    for (int64_t d = g < cap ? g : cap; d >= 1; --d) {
+        if (g % d == 0) {
+            tt = d;
+            break;
+        }
+    }
+    p->tile_tokens = tt;
+    p->tile_rows = tt * s.k;
+    p->n_tiles = s.T / tt;
+    p->dbits = bits_for(s.R);
+    p->ebits = bits_for(s.E);
+    size_t off = align_up(kHdrBytes, 256);
+    p->off_state = off;
+    off = align_up(off + (size_t)p->n_tiles * s.R * 4, 256);
+    p->off_excl = off;
+    off = align_up(off + (size_t)p->n_tiles * s.R * 4, 256);
+    p->off_wbase = off;
+    off = align_up(off + (size_t)p->n_tiles * kLayoutWaves * s.R * 4, 256);
+    p->off_ehist = off;
+    off = align_up(off + (size_t)p->n_tiles * s.E * 4, 256);
+    p->off_flags = off;
+    off = align_up(off + (size_t)s.C * kFlagStride * 4, 256);
+    p->ws_bytes = off;
+}
+
+}  // namespace ubep
+
+using namespace ubep;
+
+namespace {
+
+constexpr int64_t kMaxTiles = 1 << 16;
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+ubep_status hip_status(hipError_t e) { return e == hipSuccess ? UBEP_OK : UBEP_ERR_HIP; }
+
+// Shape check plus the tile-count limit of the layout's workspace.
+ubep_status check_and_plan(const ubep_shape* s, int dtype, Plan* p) {
+    const ubep_status st = ubep_check_shape(s, dtype);
+    if (st != UBEP_OK) return st;
+    make_plan(*s, p);
+    if (p->n_tiles > kMaxTiles) return UBEP_ERR_UNSUPPORTED;
+    return UBEP_OK;
+}
+
+ubep_status spin_ticks_for(uint64_t ns, uint64_t* ticks) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return UBEP_ERR_HIP;
+    DeviceInfo di;
+    if (device_info(dev, &di) != hipSuccess) return UBEP_ERR_HIP;
+    if (ns == 0) ns = 1000000000ull;
+    const uint64_t t = ns / 1000ull * (uint64_t)di.wall_clock_khz / 1000ull;
+    *ticks = t > 0 ? t : 1;
+    return UBEP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ubep_abi_version(void) { return UBEP_ABI_VERSION; }
+
+const char* ubep_status_str(ubep_status s) {
+    switch (s) {
+        case UBEP_OK: return "ok";
+        case UBEP_ERR_INVALID_ARG: return "invalid argument";
+        case UBEP_ERR_UNSUPPORTED: return "unsupported shape";
+        case UBEP_ERR_BAD_EXPERT_ID: return "expert id outside [0, E)";
+        case UBEP_ERR_TIMEOUT: return "ready-flag wait timed out";
+        case UBEP_ERR_HIP: return "HIP runtime error";
+        case UBEP_ERR_BAD_POSITION: return "position outside [0, T*k)";
+    }
+    return "unknown status";
+}
+
+ubep_status ubep_check_shape(const ubep_shape* s, int dtype) {
+    if (s == nullptr) return UBEP_ERR_INVALID_ARG;
+    if (dtype != UBEP_BF16 && dtype != UBEP_FP8_E4M3) return UBEP_ERR_INVALID_ARG;
+    if (s->T <= 0 || s->H <= 0 || s->E <= 0 || s->k <= 0 || s->R <= 0 || s->C <= 0)
+        return UBEP_ERR_INVALID_ARG;
+    if (s->k > s->E) return UBEP_ERR_INVALID_ARG;
+    if (s->E % s->R != 0 || s->T % s->R != 0 || s->T % s->C != 0) return UBEP_ERR_INVALID_ARG;
+    if (s->H % 8 != 0) return UBEP_ERR_INVALID_ARG;
+    if (dtype == UBEP_FP8_E4M3 && s->H % 128 != 0) return UBEP_ERR_INVALID_ARG;
+    if (s->T >= ((int64_t)1 << 30) || s->T * (int64_t)s->k >= ((int64_t)1 << 30))
+        return UBEP_ERR_INVALID_ARG;
+    if (s->H >= ((int64_t)1 << 30)) return UBEP_ERR_UNSUPPORTED;
+    if (s->k > kMaxK || s->R > kMaxR || s->E > kMaxE || s->C > kMaxC) return UBEP_ERR_UNSUPPORTED;
+    return UBEP_OK;
+}
+
+size_t ubep_workspace_bytes(const ubep_shape* s) {
+    Plan p;
+    if (check_and_plan(s, UBEP_BF16, &p) != UBEP_OK) return 0;
+    return p.ws_bytes;
+}
+
+ubep_status ubep_workspace_init(void* ws, size_t ws_bytes, hipStream_t stream) {
+    if (ws == nullptr || ws_bytes < kHdrBytes || ws_bytes % 4 != 0 || !aligned(ws, 256))
+        return UBEP_ERR_INVALID_ARG;
+    return hip_status(launch_fill_zero(ws, ws_bytes, stream));
+}
+
+ubep_status ubep_layout(const ubep_shape* s, const int32_t* topk_idx, int32_t* pos,
+                        int32_t* expert_count, int32_t* rank_count, int32_t* recv_offset,
+                        int32_t* send_offset, int32_t* chunk_offset, int32_t* recv_src, void* ws,
+                        size_t ws_bytes, hipStream_t stream) {
+    Plan p;
+    const ubep_status st = check_and_plan(s, UBEP_BF16, &p);
+    if (st != UBEP_OK) return st;
+    if (!topk_idx || !pos || !expert_count || !rank_count || !recv_offset || !send_offset || !ws)
+        return UBEP_ERR_INVALID_ARG;
+    if (ws_bytes < p.ws_bytes || !aligned(ws, 256)) return UBEP_ERR_INVALID_ARG;
+    uint64_t ticks;
+    const ubep_status ts = spin_ticks_for(0, &ticks);
+    if (ts != UBEP_OK) return ts;
+    return hip_status(launch_layout(p, topk_idx, pos, expert_count, rank_count, recv_offset,
+                                    send_offset, chunk_offset, recv_src, ws, ticks, stream));
+}
+
+ubep_status ubep_dispatch(const ubep_shape* s, int dtype, const void* x, const int32_t* pos,
+                          void* recv, float* recv_scale, void* ws, size_t ws_bytes,
+                          hipStream_t stream) {
+    Plan p;
+    const ubep_status st = check_and_plan(s, dtype, &p);
+    if (st != UBEP_OK) return st;
+    if (!x || !pos || !recv || !ws || ws_bytes < kHdrBytes) return UBEP_ERR_INVALID_ARG;
+    if (!aligned(x, 16) || !aligned(recv, 16) || !aligned(ws, 256)) return UBEP_ERR_INVALID_ARG;
+    uint32_t* status = static_cast<uint32_t*>(ws) + kHdrStatus;
+    if (dtype == UBEP_BF16) {
+        if (recv_scale != nullptr) return UBEP_ERR_INVALID_ARG;
+        return hip_status(launch_dispatch_bf16(p, x, pos, recv, status, stream));
+    }
+    if (recv_scale == nullptr || !aligned(recv_scale, 4)) return UBEP_ERR_INVALID_ARG;
+    return hip_status(launch_dispatch_fp8(p, x, pos, recv, recv_scale, status, stream));
+}
+
+ubep_status ubep_combine(const ubep_shape* s, const void* y, const int32_t* pos,
+                         const float* topk_w, void* out, void* ws, size_t ws_bytes,
+                         hipStream_t stream) {
+    Plan p;
+    const ubep_status st = check_and_plan(s, UBEP_BF16, &p);
+    if (st != UBEP_OK) return st;
+    if (!y || !pos || !topk_w || !out || !ws || ws_bytes < kHdrBytes) return UBEP_ERR_INVALID_ARG;
+    if (!aligned(y, 16) || !aligned(out, 16) || !aligned(ws, 256)) return UBEP_ERR_INVALID_ARG;
+    uint32_t* status = static_cast<uint32_t*>(ws) + kHdrStatus;
+    return hip_status(launch_combine(p, y, pos, topk_w, out, status, stream));
+}
+
+ubep_status ubep_dispatch_combine_chunked(const ubep_shape* s, const void* x, const int32_t* pos,
+                                          const float* topk_w, void* recv, void* out,
+                                          const int32_t* chunk_order, uint64_t spin_limit_ns,
+                                          uint32_t debug_flags, void* ws, size_t ws_bytes,
+                                          hipStream_t stream) {
+    Plan p;
+    const ubep_status st = check_and_plan(s, UBEP_BF16, &p);
+    if (st != UBEP_OK) return st;
+    if (!x || !pos || !topk_w || !recv || !out || !ws) return UBEP_ERR_INVALID_ARG;
+    if (ws_bytes < p.ws_bytes || !aligned(ws, 256)) return UBEP_ERR_INVALID_ARG;
+    if (!aligned(x, 16) || !aligned(recv, 16) || !aligned(out, 16)) return UBEP_ERR_INVALID_ARG;
+    if (debug_flags & ~1u) return UBEP_ERR_INVALID_ARG;
+    if (chunk_order != nullptr) {
+        bool seen[kMaxC] = {};
+        for (int32_t i = 0; i < p.C; ++i) {
+            const int32_t c = chunk_order[i];
+            if (c < 0 || c >= p.C || seen[c]) return UBEP_ERR_INVALID_ARG;
+            seen[c] = true;
+        }
+    }
+    uint64_t ticks;
+    const ubep_status ts = spin_ticks_for(spin_limit_ns, &ticks);
+    if (ts != UBEP_OK) return ts;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return UBEP_ERR_HIP;
+    return hip_status(launch_chunked(p, x, pos, topk_w, recv, out, chunk_order, ticks, debug_flags,
+                                     ws, dev, stream));
+}
+
+ubep_status ubep_get_device_status(void* ws, size_t ws_bytes, hipStream_t stream,
+                                   ubep_status* out) {
+    if (ws == nullptr || out == nullptr || ws_bytes < kHdrBytes || !aligned(ws, 256))
+        return UBEP_ERR_INVALID_ARG;
+    uint32_t v = 0;
+    uint32_t* status = static_cast<uint32_t*>(ws) + kHdrStatus;
+    if (hipStreamSynchronize(stream) != hipSuccess) return UBEP_ERR_HIP;
+    if (hipMemcpy(&v, status, sizeof(v), hipMemcpyDeviceToHost) != hipSuccess) return UBEP_ERR_HIP;
+    if (launch_clear_status(status, stream) != hipSuccess) return UBEP_ERR_HIP;
+    if (hipStreamSynchronize(stream) != hipSuccess) return UBEP_ERR_HIP;
+    *out = (ubep_status)v;
+    return UBEP_OK;
+}
+
+ubep_status ubep_identity_expert_fp8(int64_t rows, int64_t H, const uint8_t* q, const float* scale,
+                                     void* y, hipStream_t stream) {
+    if (rows < 0 || H <= 0 || H % 128 != 0 || !q || !scale || !y) return UBEP_ERR_INVALID_ARG;
+    if (!aligned(q, 16) || !aligned(y, 16) || !aligned(scale, 4)) return UBEP_ERR_INVALID_ARG;
+    if (rows == 0) return UBEP_OK;
+    return hip_status(launch_identity_fp8(rows, H, q, scale, y, stream));
+}
+
+ubep_status ubep_copy(const void* src, void* dst, size_t bytes, hipStream_t stream) {
+    if (!src || !dst || bytes % 16 != 0 || !aligned(src, 16) || !aligned(dst, 16))
+        return UBEP_ERR_INVALID_ARG;
+    if (bytes == 0) return UBEP_OK;
+    return hip_status(launch_copy(src, dst, bytes, stream));
+}
+
+}  // extern "C"

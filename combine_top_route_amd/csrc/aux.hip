@@ -1,0 +1,122 @@
+// Auxiliary kernels, not on the dispatch/combine path: the identity expert for
+// an fp8 payload, a plain 16-byte copy (bandwidth and counter calibration),
+// workspace zero-fill and status clear.
+#include <mutex>
+
+#include "launch.h"
+#include "rows.h"
+
+namespace ubep {
+
+// y[r][c] = bf16(decode(q[r][c]) * scale[r][c / 128]); each thread converts
+// 16 codes (one 16-byte load) into 16 bf16 (two 16-byte stores).
+__global__ __launch_bounds__(256) void identity_fp8_kernel(const u32x4* __restrict__ q,
+                                                           const float* __restrict__ scale,
+                                                           u32x4* __restrict__ y, int64_t rows,
+                                                           int64_t H) {
+    const int64_t per_row = H / 16;
+    const int64_t n = rows * per_row;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t r = i / per_row, g = i % per_row;
+        const float s = scale[r * (H / 128) + g / 8];
+        const u32x4 c = q[i];
+        u32x4 o[2];
+#pragma unroll
+        for (int wd = 0; wd < 4; ++wd) {
+            uint32_t b[4];
+#pragma unroll
+            for (int by = 0; by < 4; ++by) b[by] = f32_to_bf16(e4m3_to_f32((c[wd] >> (8 * by)) & 0xFFu) * s);
+            o[wd / 2][(wd % 2) * 2] = b[0] | (b[1] << 16);
+            o[wd / 2][(wd % 2) * 2 + 1] = b[2] | (b[3] << 16);
+        }
+        y[2 * i] = o[0];
+        y[2 * i + 1] = o[1];
+    }
+}
+
+__global__ __launch_bounds__(256) void copy_kernel(const u32x4* __restrict__ src,
+                                                   u32x4* __restrict__ dst, int64_t n) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    for (; i + 3 * stride < n; i += 4 * stride) {
+        const u32x4 a = src[i], b = src[i + stride], c = src[i + 2 * stride], d = src[i + 3 * stride];
+        dst[i] = a;
+        dst[i + stride] = b;
+        dst[i + 2 * stride] = c;
+        dst[i + 3 * stride] = d;
+    }
+    for (; i < n; i += stride) dst[i] = src[i];
+}
+
+__global__ __launch_bounds__(256) void fill_zero_kernel(uint32_t* p, int64_t words) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < words;
+         i += (int64_t)gridDim.x * blockDim.x)
+        p[i] = 0u;
+}
+
+__global__ void clear_status_kernel(uint32_t* status) { st_relaxed(status, 0u); }
+
+static unsigned grid_for(int64_t items, int64_t per_block, int64_t cap) {
+    int64_t g = (items + per_block - 1) / per_block;
+    if (g > cap) g = cap;
+    if (g < 1) g = 1;
+    return (unsigned)g;
+}
+
+hipError_t launch_identity_fp8(int64_t rows, int64_t H, const uint8_t* q, const float* scale,
+                               void* y, hipStream_t stream) {
+    const int64_t n = rows * (H / 16);
+    hipLaunchKernelGGL(identity_fp8_kernel, dim3(grid_for(n, 256, 65536)), dim3(256), 0, stream,
+                       reinterpret_cast<const u32x4*>(q), scale, static_cast<u32x4*>(y), rows, H);
+    return hipGetLastError();
+}
+
+hipError_t launch_copy(const void* src, void* dst, size_t bytes, hipStream_t stream) {
+    const int64_t n = (int64_t)(bytes / 16);
+    DeviceInfo di;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    e = device_info(dev, &di);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(copy_kernel, dim3(grid_for(n, 256 * 4, (int64_t)di.cus * 16)), dim3(256), 0,
+                       stream, static_cast<const u32x4*>(src), static_cast<u32x4*>(dst), n);
+    return hipGetLastError();
+}
+
+hipError_t launch_fill_zero(void* ws, size_t bytes, hipStream_t stream) {
+    const int64_t words = (int64_t)(bytes / 4);
+    hipLaunchKernelGGL(fill_zero_kernel, dim3(grid_for(words, 256, 4096)), dim3(256), 0, stream,
+                       static_cast<uint32_t*>(ws), words);
+    return hipGetLastError();
+}
+
+hipError_t launch_clear_status(uint32_t* status, hipStream_t stream) {
+    hipLaunchKernelGGL(clear_status_kernel, dim3(1), dim3(1), 0, stream, status);
+    return hipGetLastError();
+}
+
+// Immutable per-device properties, queried once per device.
+hipError_t device_info(int device, DeviceInfo* out) {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static DeviceInfo cache[kMaxDevices];
+    static bool have[kMaxDevices] = {};
+    if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!have[device]) {
+        int cus = 0, khz = 0;
+        hipError_t e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device);
+        if (e != hipSuccess) return e;
+        e = hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, device);
+        if (e != hipSuccess) return e;
+        cache[device].cus = cus;
+        cache[device].wall_clock_khz = khz > 0 ? khz : 100000;
+        have[device] = true;
+    }
+    *out = cache[device];
+    return hipSuccess;
+}
+
+}  // namespace ubep

@@ -1,0 +1,60 @@
+// Launch plan and workspace layout shared by the host API and the kernels.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "ubep.h"
+
+namespace ubep {
+
+// Implemented limits (checked by ubep_check_shape).
+constexpr int kMaxK = 32;
+constexpr int kMaxR = 1024;
+constexpr int kMaxE = 8192;
+constexpr int kMaxC = 256;
+
+// Layout kernels: 4 waves per workgroup, one tile of whole tokens per
+// workgroup, at most kTileRowsMax rows per tile.
+constexpr int kLayoutThreads = 256;
+constexpr int kLayoutWaves = 4;
+constexpr int64_t kTileRowsMax = 4096;
+
+// Workspace header: 32-bit counters, each on its own 128-byte line.
+constexpr int kHdrStatus = 0;          // device status word (ubep_status)
+constexpr int kHdrLayoutTicket = 32;   // tile ticket of the layout scan
+constexpr int kHdrFusedTicket = 64;    // task ticket of the chunk pipeline
+constexpr int kHdrFusedDone = 96;      // workgroups finished in the chunk pipeline
+constexpr size_t kHdrBytes = 512;
+constexpr int kFlagStride = 32;        // uint32 per chunk ready flag (128 bytes)
+
+// Look-back state word: a 2-bit flag above a 30-bit row count (T*k < 2^30).
+constexpr uint32_t kCountMask = (1u << 30) - 1u;
+constexpr uint32_t kFlagAggregate = 1u << 30;   // this tile's own count is known
+constexpr uint32_t kFlagInclusive = 2u << 30;   // count of this and all earlier tiles
+
+struct Plan {
+    int64_t T, H;
+    int32_t E, k, R, C;
+    int64_t rows;          // T*k
+    int32_t epr;           // experts per rank
+    int64_t tps;           // tokens per source rank
+    int64_t tpc;           // tokens per chunk
+    int64_t tile_tokens;   // tokens per layout tile; divides tps and tpc
+    int64_t tile_rows;     // tile_tokens * k
+    int64_t n_tiles;
+    int32_t dbits;         // bits to hold a rank id (0..R-1)
+    int32_t ebits;         // bits to hold an expert id (0..E-1)
+    // workspace byte offsets
+    size_t off_state;      // uint32 [n_tiles][R]   look-back state
+    size_t off_excl;       // int32  [n_tiles][R]   rows to rank d in earlier tiles
+    size_t off_wbase;      // int32  [n_tiles][4][R] rows to rank d in earlier waves of the tile
+    size_t off_ehist;      // int32  [n_tiles][E]   rows per expert in the tile
+    size_t off_flags;      // uint32 [C][kFlagStride] chunk ready flags
+    size_t ws_bytes;
+};
+
+// Host: fill `p` for a shape that passed validation.
+void make_plan(const ubep_shape& s, Plan* p);
+
+}  // namespace ubep

@@ -88,13 +88,16 @@ def layout(topk_idx: np.ndarray, E: int, R: int, C: int = 1, want_src: bool = Tr
     return out
 
 
-def dispatch_bf16(x: np.ndarray, pos: np.ndarray, n_rows: int | None = None) -> np.ndarray:
+def dispatch_bf16(x: np.ndarray, pos: np.ndarray, n_rows: int | None = None,
+                  recv: np.ndarray | None = None) -> np.ndarray:
     x = np.ascontiguousarray(x, dtype=np.uint16)
     pos = np.ascontiguousarray(pos, dtype=np.int32)
     T, H = x.shape
     k = pos.shape[1]
     n_rows = T * k if n_rows is None else n_rows
-    recv = np.zeros((n_rows, H), np.uint16)
+    if recv is None:
+        recv = np.zeros((n_rows, H), np.uint16)
+    assert recv.shape == (n_rows, H) and recv.dtype == np.uint16 and recv.flags["C_CONTIGUOUS"]
     lib().oracle_dispatch_bf16(T, H, k, _p(x), _p(pos), _p(recv))
     return recv
 
@@ -121,13 +124,16 @@ def identity_fp8(q: np.ndarray, s: np.ndarray) -> np.ndarray:
     return y
 
 
-def combine(y: np.ndarray, pos: np.ndarray, topk_w: np.ndarray) -> np.ndarray:
+def combine(y: np.ndarray, pos: np.ndarray, topk_w: np.ndarray,
+            out: np.ndarray | None = None) -> np.ndarray:
     y = np.ascontiguousarray(y, dtype=np.uint16)
     pos = np.ascontiguousarray(pos, dtype=np.int32)
     w = np.ascontiguousarray(topk_w, dtype=np.float32)
     T, k = pos.shape
     H = y.shape[1]
-    out = np.empty((T, H), np.uint16)
+    if out is None:
+        out = np.empty((T, H), np.uint16)
+    assert out.shape == (T, H) and out.dtype == np.uint16 and out.flags["C_CONTIGUOUS"]
     lib().oracle_combine(T, H, k, _p(y), _p(pos), _p(w), _p(out))
     return out
 
