@@ -36,6 +36,9 @@ void make_plan(const ubep_shape& s, Plan* p) {
     p->C = s.C;
     p->rows = s.T * s.k;
     p->epr = s.E / s.R;
+    // floor(e / epr) == umulhi(e, ceil(2^32 / epr)) whenever e * epr < 2^32
+    // (here e < E <= 8192 and epr <= 8192)
+    p->epr_magic = p->epr == 1 ? 0u : (uint32_t)((((uint64_t)1 << 32) + p->epr - 1) / p->epr);
     p->tps = s.T / s.R;
     p->tpc = s.T / s.C;
     const int64_t g = gcd64(p->tps, p->tpc);
@@ -53,15 +56,14 @@ void make_plan(const ubep_shape& s, Plan* p) {
     p->n_tiles = s.T / tt;
     p->dbits = bits_for(s.R);
     p->ebits = bits_for(s.E);
+    p->slots = s.R + s.E;
     size_t off = align_up(kHdrBytes, 256);
     p->off_state = off;
-    off = align_up(off + (size_t)p->n_tiles * s.R * 4, 256);
+    off = align_up(off + (size_t)p->n_tiles * p->slots * 8, 256);
     p->off_excl = off;
     off = align_up(off + (size_t)p->n_tiles * s.R * 4, 256);
     p->off_wbase = off;
     off = align_up(off + (size_t)p->n_tiles * kLayoutWaves * s.R * 4, 256);
-    p->off_ehist = off;
-    off = align_up(off + (size_t)p->n_tiles * s.E * 4, 256);
     p->off_flags = off;
     off = align_up(off + (size_t)s.C * kFlagStride * 4, 256);
     p->ws_bytes = off;
@@ -84,7 +86,7 @@ ubep_status check_and_plan(const ubep_shape* s, int dtype, Plan* p) {
     const ubep_status st = ubep_check_shape(s, dtype);
     if (st != UBEP_OK) return st;
     make_plan(*s, p);
-    if (p->n_tiles > kMaxTiles) return UBEP_ERR_UNSUPPORTED;
+    if (p->n_tiles > kMaxTiles || p->n_tiles * p->slots > kMaxStateWords) return UBEP_ERR_UNSUPPORTED;
     return UBEP_OK;
 }
 

@@ -6,10 +6,17 @@
 //
 // Tokens form C contiguous chunks, each split into n tasks of a few tokens.
 // A workgroup repeatedly takes the next ticket from one counter in HBM; the
-// tickets enumerate D(o0), D(o1), C(o0), D(o2), C(o1), ..., C(o_{C-1}) for the
-// host-chosen chunk order o.  A D task dispatches its tokens and then adds one
-// to its chunk's ready flag (agent-scope release); a C task of chunk c waits
-// until that flag reaches n (agent-scope acquire) and combines its tokens.
+// tickets enumerate, for the host-chosen chunk order o and a lag of L chunks,
+//   D(o0) .. D(o_{L-1}),  D(o_L) C(o0),  D(o_{L+1}) C(o1),  ...,  C(o_{C-L}) .. C(o_{C-1})
+// so a C task is claimed about L chunks after its D tasks.  L is the number of
+// chunks the resident workgroups hold in flight at once: with a smaller lag a
+// claimed C task would mostly wait on a chunk still being dispatched while
+// holding a workgroup slot.  A D task writes its rows with device-coherent
+// stores, waits for them to complete and adds one to its chunk's ready flag;
+// a C task of chunk c polls that flag until it reaches n and reads the rows
+// with device-coherent loads.  No L2 write-back or invalidate is needed (an
+// agent-scope release/acquire pair would write back / invalidate a whole
+// XCD's L2 per task).
 // Every D task of chunk c has a smaller ticket than every C task of chunk c,
 // and D tasks never wait, so each awaited task is already held by a running
 // workgroup: the pipeline cannot deadlock whatever the grid size.  Waits are
@@ -22,6 +29,7 @@
 namespace ubep {
 
 constexpr int kChunkBlock = 256;
+constexpr uint32_t kTicketBatch = 4;
 
 struct ChunkArgs {
     const u32x4* x;
@@ -35,6 +43,7 @@ struct ChunkArgs {
     int32_t k, C;
     int32_t tpt;        // tokens per task
     int32_t n;          // tasks per chunk (of each kind)
+    int32_t lag;        // chunks between a chunk's D tasks and its C tasks
     uint32_t total;     // 2 * C * n tickets
     uint64_t spin_ticks;
     uint32_t debug;
@@ -49,32 +58,44 @@ __global__ __launch_bounds__(kChunkBlock) void chunked_kernel(ChunkArgs a) {
     const int gtid = tid % G;
     uint32_t* status = &a.hdr[kHdrStatus];
 
+    // Tickets are claimed kTicketBatch at a time (one atomic per batch: the
+    // counter is a single address that every workgroup hits) and processed in
+    // order; a C task in a batch waits only on smaller tickets, held by
+    // running workgroups or done earlier in the same batch.
+    uint32_t next = 0, batch_end = 0;
     for (;;) {
-        if (tid == 0) s_ticket = add_relaxed(&a.hdr[kHdrFusedTicket], 1u);
-        __syncthreads();
-        const uint32_t ticket = s_ticket;
-        __syncthreads();
+        if (next == batch_end) {
+            if (tid == 0) s_ticket = add_relaxed(&a.hdr[kHdrFusedTicket], kTicketBatch);
+            __syncthreads();
+            next = s_ticket;
+            batch_end = next + kTicketBatch;
+            __syncthreads();
+        }
+        const uint32_t ticket = next++;
         if (ticket >= a.total) break;
 
         // decode the ticket
-        const uint32_t n = (uint32_t)a.n;
+        const uint32_t n = (uint32_t)a.n, L = (uint32_t)a.lag, C = (uint32_t)a.C;
         bool is_d;
         int32_t c;
         uint32_t idx;
-        if (ticket < n) {
+        if (ticket < L * n) {                               // the first L chunks' D tasks
             is_d = true;
-            c = a.order[0];
-            idx = ticket;
+            c = a.order[ticket / n];
+            idx = ticket % n;
         } else {
-            const uint32_t u = ticket - n, pair = u / (2u * n), r = u % (2u * n);
-            if (pair + 1u < (uint32_t)a.C) {
+            const uint32_t u = ticket - L * n;
+            const uint32_t pair = u / (2u * n);
+            if (pair < C - L) {                             // D(o_{pair+L}) then C(o_pair)
+                const uint32_t r = u % (2u * n);
                 is_d = r < n;
-                c = is_d ? a.order[pair + 1u] : a.order[pair];
+                c = is_d ? a.order[pair + L] : a.order[pair];
                 idx = is_d ? r : r - n;
-            } else {
+            } else {                                        // the last L chunks' C tasks
+                const uint32_t v = u - (C - L) * 2u * n;
                 is_d = false;
-                c = a.order[a.C - 1];
-                idx = r;
+                c = a.order[C - L + v / n];
+                idx = v % n;
             }
         }
         const int64_t c_lo = (int64_t)c * a.tpc, c_hi = c_lo + a.tpc;
@@ -84,15 +105,15 @@ __global__ __launch_bounds__(kChunkBlock) void chunked_kernel(ChunkArgs a) {
 
         if (is_d) {
             for (int64_t t = t_lo + tid / G; t < t_hi; t += TPB)
-                dispatch_row_bf16<G, VPT, false>(a.x, a.pos, a.recv, t, a.k, a.nvec, a.n_rows, gtid,
-                                                 status);
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+                dispatch_row_bf16<G, VPT, false, true>(a.x, a.pos, a.recv, t, a.k, a.nvec, a.n_rows,
+                                                       gtid, status);
+            wait_memory();             // every row of the task is at the coherent level
             __syncthreads();
-            if (tid == 0 && (a.debug & 1u) == 0u) add_release(flag, 1u);
+            if (tid == 0 && (a.debug & 1u) == 0u) add_relaxed(flag, 1u);
         } else {
             if (tid == 0) {
                 const uint64_t t0 = now_ticks();
-                while (ld_acquire(flag) < n) {
+                while (ld_relaxed(flag) < n) {
                     if (now_ticks() - t0 > a.spin_ticks) {
                         raise_status(status, UBEP_ERR_TIMEOUT);
                         break;
@@ -101,15 +122,15 @@ __global__ __launch_bounds__(kChunkBlock) void chunked_kernel(ChunkArgs a) {
                 }
             }
             __syncthreads();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
             for (int64_t t = t_lo + tid / G; t < t_hi; t += TPB)
-                combine_row<G, VPT, 8>(a.recv, a.pos, a.w, a.out, t, a.k, a.nvec, a.n_rows, gtid,
-                                       status);
+                combine_row<G, VPT, 8, true>(a.recv, a.pos, a.w, a.out, t, a.k, a.nvec, a.n_rows,
+                                             gtid, status);
         }
     }
 
     if (tid == 0) {
-        const uint32_t done = add_acq_rel(&a.hdr[kHdrFusedDone], 1u);
+        // every workgroup's final ticket claim returned before this increment
+        const uint32_t done = add_relaxed(&a.hdr[kHdrFusedDone], 1u);
         if (done == gridDim.x - 1u) {
             for (int32_t c = 0; c < a.C; ++c) st_relaxed(a.flags + (int64_t)c * kFlagStride, 0u);
             st_relaxed(&a.hdr[kHdrFusedTicket], 0u);
@@ -118,48 +139,12 @@ __global__ __launch_bounds__(kChunkBlock) void chunked_kernel(ChunkArgs a) {
     }
 }
 
-template <int G, int VPT>
-static hipError_t launch_gv(ChunkArgs& a, int device, hipStream_t stream) {
-    DeviceInfo di;
-    hipError_t e = device_info(device, &di);
-    if (e != hipSuccess) return e;
-    int per_cu = 0;
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, chunked_kernel<G, VPT>, kChunkBlock, 0);
-    if (e != hipSuccess) return e;
-    if (per_cu < 1) per_cu = 1;
-    int64_t grid = (int64_t)di.cus * per_cu;
-    if (grid > (int64_t)a.total) grid = a.total;
-    hipLaunchKernelGGL((chunked_kernel<G, VPT>), dim3((unsigned)grid), dim3(kChunkBlock), 0, stream,
-                       a);
-    return hipGetLastError();
-}
-
-template <int G>
-static hipError_t launch_g(int vpt, ChunkArgs& a, int device, hipStream_t stream) {
-    switch (vpt) {
-        case 1: return launch_gv<G, 1>(a, device, stream);
-        case 2: return launch_gv<G, 2>(a, device, stream);
-        case 3: return launch_gv<G, 3>(a, device, stream);
-        case 4: return launch_gv<G, 4>(a, device, stream);
-        case 5: return launch_gv<G, 5>(a, device, stream);
-        case 6: return launch_gv<G, 6>(a, device, stream);
-        case 7: return launch_gv<G, 7>(a, device, stream);
-        default: return launch_gv<G, 8>(a, device, stream);
-    }
-}
-
 hipError_t launch_chunked(const Plan& p, const void* x, const int32_t* pos, const float* topk_w,
                           void* recv, void* out, const int32_t* chunk_order, uint64_t spin_ticks,
                           uint32_t debug_flags, void* ws, int device, hipStream_t stream) {
     const int64_t nvec = p.H / 8;
-    int G = 256, VPT = 8;
-    for (int g = 64; g <= 256; g *= 2) {
-        if (nvec <= (int64_t)g * 8) {
-            G = g;
-            VPT = (int)((nvec + g - 1) / g);
-            break;
-        }
-    }
+    int G, VPT;
+    pick_group(nvec, &G, &VPT);
     ChunkArgs a;
     a.x = static_cast<const u32x4*>(x);
     a.pos = pos;
@@ -175,9 +160,10 @@ hipError_t launch_chunked(const Plan& p, const void* x, const int32_t* pos, cons
     a.tpc = p.tpc;
     a.k = p.k;
     a.C = p.C;
-    // tasks of 4 passes of the workgroup's token groups (8 tokens for 2 tokens per pass)
+    // a task is one pass of the workgroup's token groups (2 tokens when a
+    // group of 128 threads covers a row)
     const int64_t tpb = kChunkBlock / G;
-    int64_t tpt = tpb * 4;
+    int64_t tpt = tpb;
     if (tpt > p.tpc) tpt = p.tpc;
     a.tpt = (int32_t)tpt;
     a.n = (int32_t)((p.tpc + tpt - 1) / tpt);
@@ -185,11 +171,26 @@ hipError_t launch_chunked(const Plan& p, const void* x, const int32_t* pos, cons
     a.spin_ticks = spin_ticks;
     a.debug = debug_flags;
     for (int i = 0; i < kMaxC; ++i) a.order[i] = (int16_t)(i < p.C ? (chunk_order ? chunk_order[i] : i) : 0);
-    switch (G) {
-        case 64: return launch_g<64>(VPT, a, device, stream);
-        case 128: return launch_g<128>(VPT, a, device, stream);
-        default: return launch_g<256>(VPT, a, device, stream);
-    }
+    DeviceInfo di;
+    hipError_t e = device_info(device, &di);
+    if (e != hipSuccess) return e;
+    auto go = [&]<int GG, int VV>() -> hipError_t {
+        int per_cu = 0;
+        hipError_t err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, chunked_kernel<GG, VV>,
+                                                                      kChunkBlock, 0);
+        if (err != hipSuccess) return err;
+        if (per_cu < 1) per_cu = 1;
+        int64_t grid = (int64_t)di.cus * per_cu;
+        if (grid > (int64_t)a.total) grid = a.total;
+        // chunks in flight: every resident workgroup holds one batch of tasks
+        const int64_t window = grid * (int64_t)kTicketBatch;
+        int64_t lag = (window + a.n - 1) / a.n;
+        a.lag = (int32_t)(lag < 1 ? 1 : (lag > a.C ? a.C : lag));
+        hipLaunchKernelGGL((chunked_kernel<GG, VV>), dim3((unsigned)grid), dim3(kChunkBlock), 0,
+                           stream, a);
+        return hipGetLastError();
+    };
+    return with_group(G, VPT, go);
 }
 
 }  // namespace ubep

@@ -27,6 +27,27 @@ __device__ __forceinline__ uint64_t peers_of(uint32_t key, int bits, uint64_t ac
     return m;
 }
 
+// peers_of with the bit loop unrolled to MAXB (bits <= MAXB, uniform).
+template <int MAXB>
+__device__ __forceinline__ uint64_t peers_of_n(uint32_t key, int bits, uint64_t active) {
+    uint64_t m = active;
+#pragma unroll
+    for (int b = 0; b < MAXB; ++b) {
+        if (b < bits) {
+            const uint32_t bit = (key >> b) & 1u;
+            const uint64_t bal = __ballot(bit);
+            m &= bit ? bal : ~bal;
+        }
+    }
+    return m;
+}
+
+// Destination rank of expert e: floor(e / epr) by multiply-high with the
+// host-computed magic ceil(2^32 / epr) (exact for e * epr < 2^32).
+__device__ __forceinline__ uint32_t rank_of(uint32_t e, uint32_t magic) {
+    return magic == 0u ? e : __umulhi(e, magic);
+}
+
 // ---------------------------------------------------------------- number formats
 // bf16 is the top half of an fp32 bit pattern.
 __device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
@@ -90,6 +111,16 @@ __device__ __forceinline__ uint32_t add_release(uint32_t* p, uint32_t v) {
 }
 __device__ __forceinline__ uint32_t add_acq_rel(uint32_t* p, uint32_t v) {
     return __hip_atomic_fetch_add(p, v, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ uint64_t ld_relaxed64(const uint64_t* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_release64(uint64_t* p, uint64_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_relaxed64(uint64_t* p, uint64_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // First error wins; later ones are dropped.

@@ -36,55 +36,19 @@ __global__ __launch_bounds__(kRowBlock) void dispatch_fp8_kernel(const u32x4* __
     dispatch_row_fp8<G>(x, pos, recv8, recv_scale, t, k, H, n_rows, threadIdx.x % G, status);
 }
 
-// Smallest group (64, 128 or 256 threads) that covers a row in at most 8
-// vectors per thread; rows longer than 256*8 vectors take several passes.
-static void pick_group(int64_t nvec, int* G, int* VPT) {
-    for (int g = 64; g <= 256; g *= 2) {
-        if (nvec <= (int64_t)g * 8) {
-            *G = g;
-            *VPT = (int)((nvec + g - 1) / g);
-            return;
-        }
-    }
-    *G = 256;
-    *VPT = 8;
-}
-
-template <int G, int VPT>
-static hipError_t launch_bf16_gv(const Plan& p, const void* x, const int32_t* pos, void* recv,
-                                 uint32_t* status, hipStream_t stream) {
-    constexpr int TPB = kRowBlock / G;
-    const int64_t blocks = (p.T + TPB - 1) / TPB;
-    hipLaunchKernelGGL((dispatch_bf16_kernel<G, VPT, false>), dim3((unsigned)blocks),
-                       dim3(kRowBlock), 0, stream, static_cast<const u32x4*>(x), pos,
-                       static_cast<u32x4*>(recv), p.T, p.k, p.H / 8, p.rows, status);
-    return hipGetLastError();
-}
-
-template <int G>
-static hipError_t launch_bf16_g(int vpt, const Plan& p, const void* x, const int32_t* pos,
-                                void* recv, uint32_t* status, hipStream_t stream) {
-    switch (vpt) {
-        case 1: return launch_bf16_gv<G, 1>(p, x, pos, recv, status, stream);
-        case 2: return launch_bf16_gv<G, 2>(p, x, pos, recv, status, stream);
-        case 3: return launch_bf16_gv<G, 3>(p, x, pos, recv, status, stream);
-        case 4: return launch_bf16_gv<G, 4>(p, x, pos, recv, status, stream);
-        case 5: return launch_bf16_gv<G, 5>(p, x, pos, recv, status, stream);
-        case 6: return launch_bf16_gv<G, 6>(p, x, pos, recv, status, stream);
-        case 7: return launch_bf16_gv<G, 7>(p, x, pos, recv, status, stream);
-        default: return launch_bf16_gv<G, 8>(p, x, pos, recv, status, stream);
-    }
-}
-
 hipError_t launch_dispatch_bf16(const Plan& p, const void* x, const int32_t* pos, void* recv,
                                 uint32_t* status, hipStream_t stream) {
     int G, VPT;
     pick_group(p.H / 8, &G, &VPT);
-    switch (G) {
-        case 64: return launch_bf16_g<64>(VPT, p, x, pos, recv, status, stream);
-        case 128: return launch_bf16_g<128>(VPT, p, x, pos, recv, status, stream);
-        default: return launch_bf16_g<256>(VPT, p, x, pos, recv, status, stream);
-    }
+    auto go = [&]<int GG, int VV>() -> hipError_t {
+        constexpr int TPB = kRowBlock / GG;
+        const int64_t blocks = (p.T + TPB - 1) / TPB;
+        hipLaunchKernelGGL((dispatch_bf16_kernel<GG, VV, false>), dim3((unsigned)blocks),
+                           dim3(kRowBlock), 0, stream, static_cast<const u32x4*>(x), pos,
+                           static_cast<u32x4*>(recv), p.T, p.k, p.H / 8, p.rows, status);
+        return hipGetLastError();
+    };
+    return with_group(G, VPT, go);
 }
 
 template <int G>

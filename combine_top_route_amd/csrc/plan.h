@@ -14,10 +14,10 @@ constexpr int kMaxR = 1024;
 constexpr int kMaxE = 8192;
 constexpr int kMaxC = 256;
 
-// Layout kernels: 4 waves per workgroup, one tile of whole tokens per
-// workgroup, at most kTileRowsMax rows per tile.
-constexpr int kLayoutThreads = 256;
-constexpr int kLayoutWaves = 4;
+// Layout kernel: 8 waves per workgroup, tiles of whole tokens with at most
+// kTileRowsMax rows.
+constexpr int kLayoutThreads = 512;
+constexpr int kLayoutWaves = 8;
 constexpr int64_t kTileRowsMax = 4096;
 
 // Workspace header: 32-bit counters, each on its own 128-byte line.
@@ -25,19 +25,29 @@ constexpr int kHdrStatus = 0;          // device status word (ubep_status)
 constexpr int kHdrLayoutTicket = 32;   // tile ticket of the layout scan
 constexpr int kHdrFusedTicket = 64;    // task ticket of the chunk pipeline
 constexpr int kHdrFusedDone = 96;      // workgroups finished in the chunk pipeline
-constexpr size_t kHdrBytes = 512;
+constexpr int kHdrLayoutDone = 128;    // workgroups finished in the layout
+constexpr int kHdrLayoutEpoch = 160;   // layout calls completed (tags look-back state)
+constexpr size_t kHdrBytes = 1024;
 constexpr int kFlagStride = 32;        // uint32 per chunk ready flag (128 bytes)
 
-// Look-back state word: a 2-bit flag above a 30-bit row count (T*k < 2^30).
+// Look-back state word (64 bits): the layout call's epoch in the high half;
+// in the low half a 2-bit flag above a 30-bit row count (T*k < 2^30).  A word
+// whose epoch is not the current call's is "not published yet", so the state
+// never needs clearing between calls.
 constexpr uint32_t kCountMask = (1u << 30) - 1u;
 constexpr uint32_t kFlagAggregate = 1u << 30;   // this tile's own count is known
 constexpr uint32_t kFlagInclusive = 2u << 30;   // count of this and all earlier tiles
+constexpr int kLookbackWindow = 32;              // predecessor states read per round
+constexpr int kMaxTilesPerGroup = 256;           // tiles one layout workgroup may claim
+constexpr int kRowsPerLane = (int)(kTileRowsMax / kLayoutWaves / 64);  // ids a lane holds
+constexpr int64_t kMaxStateWords = (int64_t)1 << 26;                   // look-back state cap
 
 struct Plan {
     int64_t T, H;
     int32_t E, k, R, C;
     int64_t rows;          // T*k
     int32_t epr;           // experts per rank
+    uint32_t epr_magic;    // ceil(2^32 / epr), 0 when epr == 1: rank = umulhi(e, magic)
     int64_t tps;           // tokens per source rank
     int64_t tpc;           // tokens per chunk
     int64_t tile_tokens;   // tokens per layout tile; divides tps and tpc
@@ -46,10 +56,10 @@ struct Plan {
     int32_t dbits;         // bits to hold a rank id (0..R-1)
     int32_t ebits;         // bits to hold an expert id (0..E-1)
     // workspace byte offsets
-    size_t off_state;      // uint32 [n_tiles][R]   look-back state
-    size_t off_excl;       // int32  [n_tiles][R]   rows to rank d in earlier tiles
-    size_t off_wbase;      // int32  [n_tiles][4][R] rows to rank d in earlier waves of the tile
-    size_t off_ehist;      // int32  [n_tiles][E]   rows per expert in the tile
+    int32_t slots;         // look-back digits per tile: R ranks, then E experts
+    size_t off_state;      // uint64 [n_tiles][R+E]  look-back state
+    size_t off_excl;       // int32  [n_tiles][R]    rows to rank d in earlier tiles
+    size_t off_wbase;      // int32  [n_tiles][8][R] rows to rank d in earlier waves of the tile
     size_t off_flags;      // uint32 [C][kFlagStride] chunk ready flags
     size_t ws_bytes;
 };

@@ -18,19 +18,96 @@ __device__ __forceinline__ void store16(u32x4* p, u32x4 v) {
     }
 }
 
+// Group size G (64, 128 or 256 threads: whole waves) and vectors per thread
+// VPT for a row of `nvec` 16-byte vectors: the smallest group that covers the
+// row in at most kVptCap vectors per thread; longer rows take several passes.
+constexpr int kVptCap = 8;
+
+inline void pick_group(int64_t nvec, int* G, int* VPT) {
+    for (int g = 64; g <= 256; g *= 2) {
+        if (nvec <= (int64_t)g * kVptCap) {
+            *G = g;
+            *VPT = (int)((nvec + g - 1) / g);
+            return;
+        }
+    }
+    *G = 256;
+    *VPT = kVptCap;
+}
+
+// Calls F.template operator()<G, VPT>() for the runtime (G, VPT).
+template <typename F>
+inline hipError_t with_group(int G, int VPT, F&& f) {
+#define UBEP_VPT_CASES(GG)                                                    \
+    switch (VPT) {                                                            \
+        case 1: return f.template operator()<GG, 1>();                        \
+        case 2: return f.template operator()<GG, 2>();                        \
+        case 3: return f.template operator()<GG, 3>();                        \
+        case 4: return f.template operator()<GG, 4>();                        \
+        case 5: return f.template operator()<GG, 5>();                        \
+        case 6: return f.template operator()<GG, 6>();                        \
+        case 7: return f.template operator()<GG, 7>();                        \
+        default: return f.template operator()<GG, kVptCap>();                 \
+    }
+    switch (G) {
+        case 64: UBEP_VPT_CASES(64)
+        case 128: UBEP_VPT_CASES(128)
+        default: UBEP_VPT_CASES(256)
+    }
+#undef UBEP_VPT_CASES
+}
+
+// ---- device-coherent row access for producer/consumer hand-offs inside one
+// kernel.  A buffer resource spans exactly one row (hardware bounds check:
+// stores past it are dropped, loads past it read zero).  Cache policy sc1
+// (device scope) makes a store write through this XCD's L2 to the
+// device-coherent level and makes a load bypass non-coherent cached copies --
+// the same policy the compiler gives agent-scope atomics -- so a hand-off
+// needs only "stores complete, then flag" on one side and "flag, then loads"
+// on the other, with no L2 write-back or invalidate.
+constexpr int kCachePolicyDevice = 16;   // sc1
+constexpr int kBufferWord3 = 0x00020000; // raw 32-bit data format (gfx9 family)
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void* row, int64_t bytes) {
+    // the row address is uniform across the wave; make that explicit for the
+    // scalar resource registers
+    const uint64_t a = (uint64_t)row;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    void* base = (void*)(((uint64_t)hi << 32) | lo);
+    return __builtin_amdgcn_make_buffer_rsrc(base, 0, (int)bytes, kBufferWord3);
+}
+
+__device__ __forceinline__ void store16_device(__amdgpu_buffer_rsrc_t r, int64_t v, u32x4 x) {
+    __builtin_amdgcn_raw_buffer_store_b128(x, r, (int)(v * 16), 0, kCachePolicyDevice);
+}
+
+__device__ __forceinline__ u32x4 load16_device(__amdgpu_buffer_rsrc_t r, int64_t v) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, (int)(v * 16), 0, kCachePolicyDevice);
+}
+
+// Wait until this thread's memory operations have completed.
+__device__ __forceinline__ void wait_memory() {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 __device__ __forceinline__ bool row_ok(int32_t q, int64_t n_rows) {
     return (uint64_t)(int64_t)q < (uint64_t)n_rows;
 }
 
 // recv[pos[t][j]] = x[t] for j = 0..k-1 (bf16 bit copy, no relay buffer).
-template <int G, int VPT, bool NT>
+// COH: write the rows with device-coherent stores (see above).
+template <int G, int VPT, bool NT, bool COH = false>
 __device__ __forceinline__ void dispatch_row_bf16(const u32x4* __restrict__ x,
                                                   const int32_t* __restrict__ pos,
                                                   u32x4* __restrict__ recv, int64_t t, int32_t k,
                                                   int64_t nvec, int64_t n_rows, int gtid,
                                                   uint32_t* status) {
-    const u32x4* xr = x + t * nvec;
-    const int32_t* pr = pos + t * k;
+    const int64_t tu = __builtin_amdgcn_readfirstlane((int32_t)t);   // uniform across the wave
+    const u32x4* xr = x + tu * nvec;
+    const int32_t* pr = pos + tu * k;
     for (int64_t v0 = 0; v0 < nvec; v0 += (int64_t)G * VPT) {
         u32x4 buf[VPT];
 #pragma unroll
@@ -45,10 +122,19 @@ __device__ __forceinline__ void dispatch_row_bf16(const u32x4* __restrict__ x,
                 continue;
             }
             u32x4* dst = recv + (int64_t)q * nvec;
+            if constexpr (COH) {
+                const __amdgpu_buffer_rsrc_t rs = row_rsrc(dst, nvec * 16);
 #pragma unroll
-            for (int i = 0; i < VPT; ++i) {
-                const int64_t v = v0 + gtid + (int64_t)i * G;
-                if (v < nvec) store16<NT>(dst + v, buf[i]);
+                for (int i = 0; i < VPT; ++i) {
+                    const int64_t v = v0 + gtid + (int64_t)i * G;
+                    if (v < nvec) store16_device(rs, v, buf[i]);
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < VPT; ++i) {
+                    const int64_t v = v0 + gtid + (int64_t)i * G;
+                    if (v < nvec) store16<NT>(dst + v, buf[i]);
+                }
             }
         }
     }
@@ -66,8 +152,9 @@ __device__ __forceinline__ void dispatch_row_fp8(const u32x4* __restrict__ x,
                                                  uint32_t* status) {
     const int64_t ng = H / 16;          // 16-channel groups per row
     const int64_t nb = H / 128;         // scale blocks per row
-    const u32x4* xr = x + t * (H / 8);
-    const int32_t* pr = pos + t * k;
+    const int64_t tu = __builtin_amdgcn_readfirstlane((int32_t)t);   // uniform across the wave
+    const u32x4* xr = x + tu * (H / 8);
+    const int32_t* pr = pos + tu * k;
     for (int64_t g = gtid; g < ng; g += G) {
         const u32x4 lo = xr[2 * g], hi = xr[2 * g + 1];
         float f[16];
@@ -106,56 +193,92 @@ __device__ __forceinline__ void dispatch_row_fp8(const u32x4* __restrict__ x,
 }
 
 // out[t] = bf16(fma chain over slots 0..k-1 of topk_w[t][j] * y[pos[t][j]])
-// in fp32 from +0.0f.  Slots are loaded KB at a time so their loads are in
-// flight together; the FMAs then run in slot order.
-template <int G, int VPT, int KB>
+// in fp32 from +0.0f.  Slots are taken KB at a time: the KB row loads are
+// issued together, unconditionally, from addresses that are always valid (a
+// slot past k or with a position outside [0, T*k) reads row 0 and is skipped
+// in the chain), so no load waits behind another.  The rows of y are read
+// once, so they are loaded non-temporally (they need not displace other lines
+// from the caches).  COH: read them with device-coherent loads instead.
+// Slot metadata of one batch: the receive row to read (always valid) and
+// whether the slot takes part in the chain.
+template <int KB>
+__device__ __forceinline__ void slot_batch(const int32_t* pr, int32_t j0, int32_t k, int64_t n_rows,
+                                           int64_t (&row)[KB], bool (&use)[KB], bool* bad) {
+#pragma unroll
+    for (int jj = 0; jj < KB; ++jj) {
+        const int32_t j = j0 + jj;
+        const int32_t q = pr[j < k ? j : k - 1];
+        const bool ok = row_ok(q, n_rows);
+        *bad |= (j < k) && !ok;
+        use[jj] = (j < k) && ok;
+        row[jj] = ok ? (int64_t)q : 0;
+    }
+}
+
+// acc[c] = fma(w_j, y[row_j][v] channel c, acc[c]) for the used slots of a batch,
+// in slot order; the KB loads are issued together.
+template <int KB, bool COH>
+__device__ __forceinline__ void chain_batch(const u32x4* __restrict__ y, int64_t nvec, int64_t v,
+                                            const int64_t (&row)[KB], const bool (&use)[KB],
+                                            const float* wr, float (&acc)[8]) {
+    u32x4 r[KB];
+#pragma unroll
+    for (int jj = 0; jj < KB; ++jj) {
+        if constexpr (COH)
+            r[jj] = load16_device(row_rsrc(y + row[jj] * nvec, nvec * 16), v);
+        else
+            r[jj] = __builtin_nontemporal_load(y + row[jj] * nvec + v);
+    }
+#pragma unroll
+    for (int jj = 0; jj < KB; ++jj) {
+        if (!use[jj]) continue;
+        const float wj = wr[jj];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            acc[2 * c] = __builtin_fmaf(wj, __uint_as_float(r[jj][c] << 16), acc[2 * c]);
+            acc[2 * c + 1] = __builtin_fmaf(wj, __uint_as_float(r[jj][c] & 0xFFFF0000u), acc[2 * c + 1]);
+        }
+    }
+}
+
+template <int G, int VPT, int KB, bool COH = false>
 __device__ __forceinline__ void combine_row(const u32x4* __restrict__ y,
                                             const int32_t* __restrict__ pos,
                                             const float* __restrict__ w, u32x4* __restrict__ out,
-                                            int64_t t, int32_t k, int64_t nvec, int64_t n_rows,
+                                            int64_t t_in, int32_t k, int64_t nvec, int64_t n_rows,
                                             int gtid, uint32_t* status) {
+    // a group is whole waves, so the token is uniform across the wave: say so,
+    // which turns the slot metadata reads into scalar loads
+    const int64_t t = __builtin_amdgcn_readfirstlane((int32_t)t_in);
     const int32_t* pr = pos + t * k;
     const float* wr = w + t * k;
+    bool bad = false;
+    int64_t row0[KB];
+    bool use0[KB];
+    slot_batch<KB>(pr, 0, k, n_rows, row0, use0, &bad);
     for (int64_t v0 = 0; v0 < nvec; v0 += (int64_t)G * VPT) {
 #pragma unroll
         for (int i = 0; i < VPT; ++i) {
-            const int64_t v = v0 + gtid + (int64_t)i * G;
-            if (v >= nvec) continue;
+            const int64_t v_raw = v0 + gtid + (int64_t)i * G;
+            const bool v_ok = v_raw < nvec;
+            const int64_t v = v_ok ? v_raw : 0;
             float acc[8];
 #pragma unroll
             for (int c = 0; c < 8; ++c) acc[c] = 0.0f;
-            for (int32_t j0 = 0; j0 < k; j0 += KB) {
-                u32x4 r[KB];
-                bool ok[KB];
-#pragma unroll
-                for (int jj = 0; jj < KB; ++jj) {
-                    const int32_t j = j0 + jj;
-                    ok[jj] = false;
-                    if (j < k) {
-                        const int32_t q = pr[j];
-                        ok[jj] = row_ok(q, n_rows);
-                        if (ok[jj]) r[jj] = y[(int64_t)q * nvec + v];
-                        else if (v == gtid) raise_status(status, UBEP_ERR_BAD_POSITION);
-                    }
-                }
-#pragma unroll
-                for (int jj = 0; jj < KB; ++jj) {
-                    if (!ok[jj]) continue;
-                    const float wj = wr[j0 + jj];
-#pragma unroll
-                    for (int c = 0; c < 4; ++c) {
-                        acc[2 * c] = __builtin_fmaf(wj, __uint_as_float(r[jj][c] << 16), acc[2 * c]);
-                        acc[2 * c + 1] =
-                            __builtin_fmaf(wj, __uint_as_float(r[jj][c] & 0xFFFF0000u), acc[2 * c + 1]);
-                    }
-                }
+            chain_batch<KB, COH>(y, nvec, v, row0, use0, wr, acc);
+            for (int32_t j0 = KB; j0 < k; j0 += KB) {     // k > KB: later batches
+                int64_t row[KB];
+                bool use[KB];
+                slot_batch<KB>(pr, j0, k, n_rows, row, use, &bad);
+                chain_batch<KB, COH>(y, nvec, v, row, use, wr + j0, acc);
             }
             u32x4 o;
 #pragma unroll
             for (int c = 0; c < 4; ++c) o[c] = f32_to_bf16(acc[2 * c]) | (f32_to_bf16(acc[2 * c + 1]) << 16);
-            out[t * nvec + v] = o;
+            if (v_ok) out[t * nvec + v] = o;
         }
     }
+    if (bad && gtid == 0) raise_status(status, UBEP_ERR_BAD_POSITION);
 }
 
 }  // namespace ubep
