@@ -115,6 +115,29 @@ def cpu_baseline(w, reps: int) -> dict:
             "host_cores_available": len(os.sched_getaffinity(0))}
 
 
+def copy_reference(nbytes: int, reps: int) -> int:
+    """Time ubep_copy on `nbytes` bytes (src and dst distinct, 16-byte multiple)."""
+    import torch
+
+    import combine_top_route_amd as ubep
+    nbytes -= nbytes % 16
+    src = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    st = torch.cuda.current_stream()
+    ubep.ubep_copy(src, dst, nbytes, st)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    ev[0].record(st)
+    for i in range(reps):
+        ubep.ubep_copy(src, dst, nbytes, st)
+        ev[i + 1].record(st)
+    torch.cuda.synchronize()
+    us = statistics.median(ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(reps))
+    print(json.dumps({"copy_bytes": nbytes, "reps": reps, "us": round(us, 2),
+                      "GBs": round(2 * nbytes / us / 1e3, 1)}), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -126,6 +149,9 @@ def main(argv=None):
                     help="scrub the 256 MB memory-side cache between steps (outside the timing)")
     ap.add_argument("--cpu-reps", type=int, default=7)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="only run the plain 16-byte copy kernel on this many bytes (the "
+                         "reference for scaling hardware traffic counters) and exit")
     args = ap.parse_args(argv)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -139,6 +165,9 @@ def main(argv=None):
     import combine_top_route_amd as ubep
     from combine_top_route_amd.buffers import alloc_buffers
     from workloads import DEFAULT_BENCH, make_config
+
+    if args.copy_bytes:
+        return copy_reference(args.copy_bytes, max(args.steps, 1))
 
     name = args.workload or DEFAULT_BENCH
     w = make_config(name)
