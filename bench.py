@@ -184,44 +184,79 @@ def main(argv=None):
     chunk_off = b.chunk_offset if s.C > 1 else None
     scrub = torch.empty(512 << 20, dtype=torch.uint8, device="cuda") if args.cold else None
 
-    def step(ev):
-        ev[0].record(stream)
-        ubep.ubep_layout(sd, b.topk_idx, b.pos, b.expert_count, b.rank_count, b.recv_offset,
-                         b.send_offset, chunk_off, None, b.ws, stream)
-        ev[1].record(stream)
-        if args.mode == "chunked":
+    calls = ["layout"] + (["chunked"] if args.mode == "chunked" else ["dispatch", "combine"])
+
+    def call(name):
+        if name == "layout":
+            ubep.ubep_layout(sd, b.topk_idx, b.pos, b.expert_count, b.rank_count, b.recv_offset,
+                             b.send_offset, chunk_off, None, b.ws, stream)
+        elif name == "chunked":
             ubep.ubep_dispatch_combine_chunked(sd, b.x, b.pos, b.topk_w, b.recv, b.out, None,
                                                b.ws, stream=stream)
-            ev[2].record(stream)
-            ev[3].record(stream)
-            ev[4].record(stream)
-            return
-        ubep.ubep_dispatch(sd, dtype, b.x, b.pos, b.recv, b.recv_scale, b.ws, stream)
-        ev[2].record(stream)
-        if fp8:   # identity expert: between the timed calls, excluded from the step
-            ubep.ubep_identity_expert_fp8(s.T * s.k, s.H, b.recv, b.recv_scale, b.y, stream)
-        ev[3].record(stream)
-        ubep.ubep_combine(sd, b.y, b.pos, b.topk_w, b.out, b.ws, stream)
-        ev[4].record(stream)
+        elif name == "dispatch":
+            ubep.ubep_dispatch(sd, dtype, b.x, b.pos, b.recv, b.recv_scale, b.ws, stream)
+        else:
+            ubep.ubep_combine(sd, b.y, b.pos, b.topk_w, b.out, b.ws, stream)
 
-    def new_events():
-        return [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+    def ev():
+        return torch.cuda.Event(enable_timing=True)
+
+    def step(marks):
+        """One step.  `marks` maps a point ('start', 'end', or '<call>.before' /
+        '<call>.after') to an event recorded there on the launch stream.  The
+        fp8 identity expert runs between dispatch and combine and is excluded
+        by the 'combine.before' mark."""
+        if "start" in marks:
+            marks["start"].record(stream)
+        for name in calls:
+            if name + ".before" in marks:
+                marks[name + ".before"].record(stream)
+            call(name)
+            if name + ".after" in marks:
+                marks[name + ".after"].record(stream)
+            if name == "dispatch" and fp8:
+                if "identity.before" in marks:
+                    marks["identity.before"].record(stream)
+                ubep.ubep_identity_expert_fp8(s.T * s.k, s.H, b.recv, b.recv_scale, b.y, stream)
+                if "identity.after" in marks:
+                    marks["identity.after"].record(stream)
+        if "end" in marks:
+            marks["end"].record(stream)
 
     for _ in range(args.warmup):
-        step(new_events())
+        step({})
     torch.cuda.synchronize()
     st = ubep.ubep_get_device_status(b.ws)
     if st != ubep.OK:
         print(f"device status after warm-up: {ubep.STATUS_NAMES.get(st, st)}", file=sys.stderr)
         return 1
 
-    evs = [new_events() for _ in range(args.steps)]
+    # untimed calibration: every call bracketed, to find the dominant kernel
+    cal = []
+    for _ in range(5):
+        m = {f"{n}.{w_}": ev() for n in calls for w_ in ("before", "after")}
+        step(m)
+        cal.append(m)
+    torch.cuda.synchronize()
+    per_call = {n: statistics.fmean(m[n + ".before"].elapsed_time(m[n + ".after"]) for m in cal)
+                for n in calls}
+    dom = max((n for n in calls if n != "layout"), key=lambda n: per_call[n])
+
+    # timed region: events at step start / end, around the dominant kernel, and
+    # around the fp8 identity expert (subtracted)
+    marks = []
+    for _ in range(args.steps):
+        m = {"start": ev(), "end": ev(), dom + ".before": ev(), dom + ".after": ev()}
+        if fp8:
+            m["identity.before"] = ev()
+            m["identity.after"] = ev()
+        marks.append(m)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     for i in range(args.steps):
         if scrub is not None:
             scrub.zero_()
-        step(evs[i])
+        step(marks[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     st = ubep.ubep_get_device_status(b.ws)
@@ -229,20 +264,17 @@ def main(argv=None):
         print(f"device status after timing: {ubep.STATUS_NAMES.get(st, st)}", file=sys.stderr)
         return 1
 
-    lay = [e[0].elapsed_time(e[1]) for e in evs]
-    dis = [e[1].elapsed_time(e[2]) for e in evs]
-    com = [e[3].elapsed_time(e[4]) for e in evs]
-    step_ms = [a + d + c for a, d, c in zip(lay, dis, com)]
+    step_ms = []
+    for m in marks:
+        t = m["start"].elapsed_time(m["end"])
+        if fp8:
+            t -= m["identity.before"].elapsed_time(m["identity.after"])
+        step_ms.append(t)
+    dom_ms = statistics.fmean(m[dom + ".before"].elapsed_time(m[dom + ".after"]) for m in marks)
     ms = statistics.fmean(step_ms)
     nb = algorithmic_bytes(sd, fp8)
     gbs = nb["total"] / (ms * 1e-3) / 1e9
-
-    if args.mode == "chunked":
-        dom, dom_ms, dom_bytes = "chunked", statistics.fmean(dis), nb["dispatch"] + nb["combine"]
-    elif statistics.fmean(dis) >= statistics.fmean(com):
-        dom, dom_ms, dom_bytes = "dispatch", statistics.fmean(dis), nb["dispatch"]
-    else:
-        dom, dom_ms, dom_bytes = "combine", statistics.fmean(com), nb["combine"]
+    dom_bytes = nb["dispatch"] + nb["combine"] if dom == "chunked" else nb[dom]
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
     traffic = read_counters(dom, name)
 
@@ -266,9 +298,9 @@ def main(argv=None):
         "pct_of_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
         "tokens_per_s": round(s.T / (ms * 1e-3), 1),
         "bytes_per_step": nb["total"],
-        "ms": {"layout": round(statistics.fmean(lay), 5), "dispatch": round(statistics.fmean(dis), 5),
-               "combine": round(statistics.fmean(com), 5),
-               "step_median": round(statistics.median(step_ms), 5)},
+        "ms": {"step_median": round(statistics.median(step_ms), 5),
+               "dominant_kernel_timed": round(dom_ms, 5),
+               "per_call_untimed_calibration": {n: round(v, 5) for n, v in per_call.items()}},
         "wall_ms_per_step": round(1e3 * wall / args.steps, 5),
         "rank_skew_max_over_mean": round(float(rc.max() / rc.mean()), 3),
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 2),
