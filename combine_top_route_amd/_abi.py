@@ -59,6 +59,7 @@ def lib() -> C.CDLL:
             "ubep_workspace_bytes": ([S], SZ),
             "ubep_workspace_init": ([P, SZ, P], C.c_int),
             "ubep_layout": ([S, P, P, P, P, P, P, P, P, P, SZ, P], C.c_int),
+            "ubep_layout_dispatch": ([S, P, P, P, P, P, P, P, P, P, P, P, SZ, P], C.c_int),
             "ubep_dispatch": ([S, C.c_int, P, P, P, P, P, SZ, P], C.c_int),
             "ubep_combine": ([S, P, P, P, P, P, SZ, P], C.c_int),
             "ubep_dispatch_combine_chunked": ([S, P, P, P, P, P, P, U64, U32, P, SZ, P], C.c_int),
@@ -137,6 +138,16 @@ def ubep_layout(shape, topk_idx, pos, expert_count, rank_count, recv_offset, sen
                              _ptr(rank_count), _ptr(recv_offset), _ptr(send_offset),
                              _ptr(chunk_offset), _ptr(recv_src), _ptr(ws), _nbytes(ws),
                              _stream(stream)), "ubep_layout")
+
+
+def ubep_layout_dispatch(shape, topk_idx, x, pos, expert_count, rank_count, recv_offset,
+                         send_offset, chunk_offset, recv_src, recv, ws, stream=None):
+    s = _shape(shape)
+    _check(lib().ubep_layout_dispatch(C.byref(s), _ptr(topk_idx), _ptr(x), _ptr(pos),
+                                      _ptr(expert_count), _ptr(rank_count), _ptr(recv_offset),
+                                      _ptr(send_offset), _ptr(chunk_offset), _ptr(recv_src),
+                                      _ptr(recv), _ptr(ws), _nbytes(ws), _stream(stream)),
+           "ubep_layout_dispatch")
 
 
 def ubep_dispatch(shape, dtype, x, pos, recv, recv_scale, ws, stream=None):

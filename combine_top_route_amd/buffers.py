@@ -75,9 +75,17 @@ def alloc_buffers(shape: dict, dtype: int = _abi.BF16, device="cuda", x_bits=Non
     )
 
 
-def run_path(b: Buffers, stream=None, chunked: bool = False, chunk_order=None):
-    """Layout, dispatch, identity expert, combine on the buffers (library calls)."""
+def run_path(b: Buffers, stream=None, chunked: bool = False, chunk_order=None, fused: bool = False):
+    """Layout, dispatch, identity expert, combine on the buffers (library calls).
+    fused: layout and dispatch in one launch (bf16 payload, not chunked)."""
     s = b.shape
+    if fused and not chunked and b.dtype == _abi.BF16:
+        _abi.ubep_layout_dispatch(s, b.topk_idx, b.x, b.pos, b.expert_count, b.rank_count,
+                                  b.recv_offset, b.send_offset,
+                                  b.chunk_offset if s["C"] > 1 else None, b.recv_src, b.recv,
+                                  b.ws, stream)
+        _abi.ubep_combine(s, b.y, b.pos, b.topk_w, b.out, b.ws, stream)
+        return
     _abi.ubep_layout(s, b.topk_idx, b.pos, b.expert_count, b.rank_count, b.recv_offset,
                      b.send_offset, b.chunk_offset if s["C"] > 1 else None, b.recv_src, b.ws,
                      stream)

@@ -165,6 +165,27 @@ ubep_status ubep_layout(const ubep_shape* s, const int32_t* topk_idx, int32_t* p
                                     send_offset, chunk_offset, recv_src, ws, ticks, stream));
 }
 
+ubep_status ubep_layout_dispatch(const ubep_shape* s, const int32_t* topk_idx, const void* x,
+                                 int32_t* pos, int32_t* expert_count, int32_t* rank_count,
+                                 int32_t* recv_offset, int32_t* send_offset, int32_t* chunk_offset,
+                                 int32_t* recv_src, void* recv, void* ws, size_t ws_bytes,
+                                 hipStream_t stream) {
+    Plan p;
+    const ubep_status st = check_and_plan(s, UBEP_BF16, &p);
+    if (st != UBEP_OK) return st;
+    if (!topk_idx || !x || !pos || !expert_count || !rank_count || !recv_offset || !send_offset ||
+        !recv || !ws)
+        return UBEP_ERR_INVALID_ARG;
+    if (ws_bytes < p.ws_bytes || !aligned(ws, 256)) return UBEP_ERR_INVALID_ARG;
+    if (!aligned(x, 16) || !aligned(recv, 16)) return UBEP_ERR_INVALID_ARG;
+    uint64_t ticks;
+    const ubep_status ts = spin_ticks_for(0, &ticks);
+    if (ts != UBEP_OK) return ts;
+    return hip_status(launch_layout_dispatch(p, topk_idx, x, pos, expert_count, rank_count,
+                                             recv_offset, send_offset, chunk_offset, recv_src, recv,
+                                             ws, ticks, stream));
+}
+
 ubep_status ubep_dispatch(const ubep_shape* s, int dtype, const void* x, const int32_t* pos,
                           void* recv, float* recv_scale, void* ws, size_t ws_bytes,
                           hipStream_t stream) {

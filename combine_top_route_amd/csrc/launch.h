@@ -14,6 +14,14 @@ hipError_t launch_layout(const Plan& p, const int32_t* idx, int32_t* pos, int32_
                          int32_t* chunk_offset, int32_t* recv_src, void* ws, uint64_t spin_ticks,
                          hipStream_t stream);
 
+int64_t layout_workers(const Plan& p, int cus);
+
+hipError_t launch_layout_dispatch(const Plan& p, const int32_t* idx, const void* x, int32_t* pos,
+                                  int32_t* expert_count, int32_t* rank_count, int32_t* recv_offset,
+                                  int32_t* send_offset, int32_t* chunk_offset, int32_t* recv_src,
+                                  void* recv, void* ws, uint64_t spin_ticks, hipStream_t stream);
+bool layout_fits_one_group(const Plan& p);
+
 hipError_t launch_dispatch_bf16(const Plan& p, const void* x, const int32_t* pos, void* recv,
                                 uint32_t* status, hipStream_t stream);
 

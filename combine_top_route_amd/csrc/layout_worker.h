@@ -1,0 +1,434 @@
+// The multi-workgroup dispatch layout ("NJU x Huawei UBEP: Reengineering MoE
+// Expert Parallelism", sections "BSP Serialization" and "Kernel
+// Decomposition"), as a device-side worker that a kernel runs in some or all
+// of its workgroups.  NW is the number of waves per workgroup.
+//
+// No memory fences: every value one workgroup passes to another travels
+// inside a self-contained 64-bit state word (call epoch | flag | count),
+// written and read with agent-scope atomics.  Rows (t, j) are cut into tiles
+// of whole tokens; a tile never straddles a source-rank or chunk boundary.
+// Each tile has R + E "digits": one per destination rank, one per expert.
+//
+// Phase A -- the worker takes tiles from a ticket counter, in order:
+//   * each wave loads all of its ids in one burst, then counts per-wave rank
+//     histograms and the tile's expert histogram with LDS atomics;
+//   * publishes the tile's per-digit aggregate, computes the in-tile stable
+//     ranks (ballot peer masks per 64-row step, per-wave bases across waves)
+//     while predecessors publish, then looks back over earlier tiles'
+//     published words, 32 predecessors per round (decoupled look-back), and
+//     publishes the inclusive count.  Tiles are handed out in order, so every
+//     awaited tile is held by a running workgroup that publishes its
+//     aggregate without waiting: no grid barrier, no co-residency assumption;
+//   * a tile's exclusive prefix at a source-rank / chunk boundary is a row of
+//     send_offset / chunk_offset.
+// Phase B -- after the ticket counter runs dry, the worker waits for the last
+//   tile's inclusive words (the totals; everything awaited is already
+//   claimed), scans the rank totals into recv_offset and writes pos /
+//   recv_src for its tiles.  Workgroup 0 of the workers writes the totals.
+// Words of an older epoch read as "not yet published", so nothing is cleared
+// between calls; the kernel's last workgroup resets the tickets and advances
+// the epoch.
+#pragma once
+
+#include "device_common.h"
+
+namespace ubep {
+
+struct LayoutArgs {
+    const int32_t* idx;
+    int32_t* pos;
+    int32_t* expert_count;
+    int32_t* rank_count;
+    int32_t* recv_offset;
+    int32_t* send_offset;
+    int32_t* chunk_offset;   // may be null
+    int32_t* recv_src;       // may be null
+    uint32_t* hdr;
+    uint64_t* state;         // [n_tiles][R + E]
+    int32_t* excl;           // [n_tiles][R]
+    int32_t* wbase;          // [n_tiles][NW][R]
+    Plan p;
+    uint64_t spin_ticks;
+};
+
+// LDS of one worker, carved from the kernel's dynamic shared memory.
+struct LayoutLds {
+    int32_t* wh;      // [NW][R] per-wave rank counts, then running bases
+    int32_t* eh;      // [E]     tile expert counts
+    int32_t* cnt;     // [R]     tile rank counts, then rank totals
+    int32_t* excl;    // [R]     rows to rank d before the last claimed tile
+    int32_t* off;     // [R]     recv_offset
+    uint32_t* tiles;  // [kMaxTilesPerGroup] tiles this workgroup claimed
+    int32_t* tmp;     // [NW]
+    uint32_t* ticket; // [1]
+};
+
+inline int64_t layout_lds_bytes(const Plan& p, int nw) {
+    return 4 * ((int64_t)nw * p.R + p.E + 3 * (int64_t)p.R + kMaxTilesPerGroup + nw + 1);
+}
+
+__device__ __forceinline__ LayoutLds carve_lds(int32_t* base, const Plan& p, int nw) {
+    LayoutLds L;
+    L.wh = base;
+    L.eh = L.wh + nw * p.R;
+    L.cnt = L.eh + p.E;
+    L.excl = L.cnt + p.R;
+    L.off = L.excl + p.R;
+    L.tiles = reinterpret_cast<uint32_t*>(L.off + p.R);
+    L.tmp = reinterpret_cast<int32_t*>(L.tiles + kMaxTilesPerGroup);
+    L.ticket = reinterpret_cast<uint32_t*>(L.tmp + nw);
+    return L;
+}
+
+// LR: ids a lane holds for one tile (tiles of at most NW * 64 * LR rows);
+// the default covers kTileRowsMax.
+template <int NW>
+constexpr int max_lane_rows() { return (int)(kTileRowsMax / NW / 64); }
+
+// Rows of the tile owned by wave w: [lo, hi).
+template <int NW>
+__device__ __forceinline__ void wave_rows(const Plan& p, int w, int64_t* lo, int64_t* hi) {
+    const int64_t per_wave = (p.tile_rows + NW - 1) / NW;
+    *lo = w * per_wave;
+    *hi = *lo + per_wave < p.tile_rows ? *lo + per_wave : p.tile_rows;
+}
+
+// Load the wave's expert ids in one burst: ev[i] holds row lo + 64 i + lane
+// (loads are unconditional, from clamped rows, so all are in flight at once;
+// entries past the wave's rows are unused).
+template <int NW, int LR>
+__device__ __forceinline__ void load_ids(const LayoutArgs& a, int64_t tile, int32_t (&ev)[LR]) {
+    const Plan& p = a.p;
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    int64_t lo, hi;
+    wave_rows<NW>(p, w, &lo, &hi);
+    const int32_t* src = a.idx + tile * p.tile_rows;
+#pragma unroll
+    for (int i = 0; i < LR; ++i) {
+        const int64_t r = lo + 64 * i + lane;
+        ev[i] = src[r < p.tile_rows ? r : p.tile_rows - 1];
+    }
+}
+
+// Ids outside [0, E) are reported and treated as expert 0.
+template <int NW, int LR>
+__device__ __forceinline__ void check_ids(const Plan& p, int32_t (&ev)[LR], bool* bad) {
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    int64_t lo, hi;
+    wave_rows<NW>(p, w, &lo, &hi);
+#pragma unroll
+    for (int i = 0; i < LR; ++i) {
+        if ((uint32_t)ev[i] >= (uint32_t)p.E) {
+            if (lo + 64 * i + lane < hi) *bad = true;
+            ev[i] = 0;
+        }
+    }
+}
+
+// wh[w*R + d] = rows of wave w with rank d; eh[e] = rows of the tile with
+// expert e.  Counting needs no order, so plain LDS atomics do it (a hot key
+// under skew only serialises its own lanes).
+template <int NW, int LR>
+__device__ __forceinline__ void tile_histograms(const Plan& p, const int32_t (&ev)[LR],
+                                                int32_t* wh, int32_t* eh) {
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    int64_t lo, hi;
+    wave_rows<NW>(p, w, &lo, &hi);
+#pragma unroll
+    for (int i = 0; i < LR; ++i) {
+        if (lo + 64 * i >= hi) break;                      // uniform across the wave
+        if (lo + 64 * i + lane < hi) {
+            const uint32_t e = (uint32_t)ev[i];
+            atomicAdd(&wh[w * p.R + rank_of(e, p.epr_magic)], 1);
+            atomicAdd(&eh[e], 1);
+        }
+    }
+}
+
+// Stable ranking inside a tile: base[w*R + d] holds the value of wave w's
+// first row with rank d; every row gets base + (rows before it in the wave
+// with rank d), and base advances.  Ballot peer masks give the order among
+// equal ranks inside a 64-row step; steps run in row order.
+template <int NW, int LR>
+__device__ __forceinline__ void tile_ranks(const Plan& p, const int32_t (&ev)[LR],
+                                           int32_t* base, int32_t (&rank)[LR]) {
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    int64_t lo, hi;
+    wave_rows<NW>(p, w, &lo, &hi);
+#pragma unroll
+    for (int i = 0; i < LR; ++i) {
+        rank[i] = 0;
+        if (lo + 64 * i >= hi) continue;                   // uniform across the wave
+        const bool act = lo + 64 * i + lane < hi;
+        const uint32_t d = rank_of((uint32_t)ev[i], p.epr_magic);
+        const uint64_t pd = peers_of_n<10>(d, p.dbits, __ballot(act));
+        const uint64_t before = pd & lanemask_lt();
+        if (act) {
+            const int32_t b = base[w * p.R + d];
+            rank[i] = b + (int32_t)__popcll(before);
+            if (before == 0) base[w * p.R + d] = b + (int32_t)__popcll(pd);
+        }
+    }
+}
+
+// pos (and recv_src) of the tile's rows.  COH: pos is written with
+// device-coherent stores, for consumers in other workgroups of this kernel.
+template <int NW, int LR, bool COH>
+__device__ __forceinline__ void store_positions(const LayoutArgs& a, int64_t tile,
+                                                const int32_t (&q)[LR], bool* bad_pos) {
+    const Plan& p = a.p;
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int64_t row0 = tile * p.tile_rows;
+    int64_t lo, hi;
+    wave_rows<NW>(p, w, &lo, &hi);
+#pragma unroll
+    for (int i = 0; i < LR; ++i) {
+        const int64_t r = lo + 64 * i + lane;
+        if (r >= hi) continue;
+        if constexpr (COH)
+            __hip_atomic_store(a.pos + row0 + r, q[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        else
+            a.pos[row0 + r] = q[i];
+        // q is in range whenever the scan completed; guard the scatter anyway
+        if ((uint32_t)q[i] < (uint32_t)p.rows) {
+            if (a.recv_src != nullptr) a.recv_src[q[i]] = (int32_t)(row0 + r);
+        } else {
+            *bad_pos = true;
+        }
+    }
+}
+
+__device__ __forceinline__ uint64_t state_word(uint32_t epoch, uint32_t flag, int32_t count) {
+    return ((uint64_t)epoch << 32) | flag | (uint32_t)count;
+}
+
+// Count of digit `slot` in tiles before `tile`: walk back over published
+// words, a window of W predecessors per round, adding aggregates until an
+// inclusive count is found.  A predecessor that has not published yet stalls
+// the walk at that point until it does (bounded by spin_ticks).
+template <int W>
+__device__ __forceinline__ int32_t look_back(const LayoutArgs& a, int64_t tile, int32_t slot,
+                                             uint32_t epoch, bool* timed_out) {
+    const int32_t S = a.p.slots;
+    int32_t excl = 0;
+    int64_t j = tile - 1;
+    const uint64_t t0 = now_ticks();
+    while (j >= 0) {
+        uint64_t v[W];
+#pragma unroll
+        for (int i = 0; i < W; ++i)
+            v[i] = (j - i >= 0) ? ld_relaxed64(a.state + (j - i) * S + slot) : 0ull;
+        int consumed = 0;
+        bool done = false, stall = false;
+#pragma unroll
+        for (int i = 0; i < W; ++i) {
+            if (done || stall) continue;
+            if (j - i < 0) {
+                done = true;
+                continue;
+            }
+            const uint32_t tag = (uint32_t)(v[i] >> 32), lo = (uint32_t)v[i];
+            const uint32_t f = lo & ~kCountMask;
+            if (tag != epoch || f == 0u) {
+                stall = true;
+                continue;
+            }
+            excl += (int32_t)(lo & kCountMask);
+            consumed = i + 1;
+            if (f == kFlagInclusive) done = true;
+        }
+        j -= consumed;
+        if (done) break;
+        if (stall) {
+            if (now_ticks() - t0 > a.spin_ticks) {
+                *timed_out = true;
+                break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+        }
+    }
+    return excl;
+}
+
+// Wait for the inclusive word of digit `slot` of the last tile.
+__device__ __forceinline__ int32_t wait_total(const LayoutArgs& a, int32_t slot, uint32_t epoch,
+                                              bool* timed_out) {
+    const uint64_t* w = a.state + (a.p.n_tiles - 1) * a.p.slots + slot;
+    const uint64_t t0 = now_ticks();
+    for (;;) {
+        const uint64_t v = ld_relaxed64(w);
+        if ((uint32_t)(v >> 32) == epoch && ((uint32_t)v & ~kCountMask) == kFlagInclusive)
+            return (int32_t)((uint32_t)v & kCountMask);
+        if (now_ticks() - t0 > a.spin_ticks) {
+            *timed_out = true;
+            return 0;
+        }
+        __builtin_amdgcn_s_sleep(1);
+    }
+}
+
+// One worker workgroup (worker `wid` of `nw_workers`): phases A and B for
+// the tiles it claims.  Worker 0 writes the totals.  Returns once this
+// workgroup's pos / recv_src are stored (COH_POS: with device-coherent stores).
+template <int NW, int LR, bool COH_POS, int W = kLookbackWindow>
+__device__ __forceinline__ void layout_worker(const LayoutArgs& a, const LayoutLds& L, uint32_t epoch,
+                                              uint32_t wid, uint32_t nw_workers) {
+    const bool leader = wid == 0;
+    constexpr int T_ = NW * 64;
+    const Plan& p = a.p;
+    const int tid = threadIdx.x;
+    const int32_t R = p.R, E = p.E, S = p.slots;
+    bool bad = false, bad_pos = false, timed_out = false;
+    uint32_t n_mine = 0;
+    int32_t ev[LR];                                  // ids of the last claimed tile
+    int32_t lrank[LR];                               // their ranks inside the tile
+
+    // ---------------- phase A: counts, in-tile ranks and look-back, tile by tile
+    // (the launch guarantees workers * kMaxTilesPerGroup >= n_tiles; a full
+    // tile list stops claiming)
+    for (;;) {
+        if (n_mine >= (uint32_t)kMaxTilesPerGroup) break;
+        if (tid == 0) *L.ticket = add_relaxed(&a.hdr[kHdrLayoutTicket], 1u);
+        // the ticket is usually this guess: fetch that tile's ids while the
+        // ticket is in flight, refetch below if the guess was wrong
+        const uint32_t guess = wid + n_mine * nw_workers;
+        int32_t nv[LR];
+        if (guess < (uint64_t)p.n_tiles) load_ids<NW, LR>(a, guess, nv);
+        for (int i = tid; i < NW * R; i += T_) L.wh[i] = 0;
+        for (int i = tid; i < E; i += T_) L.eh[i] = 0;
+        __syncthreads();
+        const uint32_t tile = *L.ticket;
+        if (tile >= (uint64_t)p.n_tiles) break;
+        if (tile != guess) load_ids<NW, LR>(a, tile, nv);
+#pragma unroll
+        for (int i = 0; i < LR; ++i) ev[i] = nv[i];
+        check_ids<NW, LR>(p, ev, &bad);
+        if (tid == 0) L.tiles[n_mine] = tile;
+        ++n_mine;
+        tile_histograms<NW, LR>(p, ev, L.wh, L.eh);
+        __syncthreads();
+
+        // wave bases (kept for a later re-rank), tile aggregates, publish
+        int32_t* wb = a.wbase + (int64_t)tile * NW * R;
+        for (int32_t d = tid; d < R; d += T_) {
+            int32_t run = 0;
+#pragma unroll
+            for (int v = 0; v < NW; ++v) {
+                const int32_t c = L.wh[v * R + d];
+                L.wh[v * R + d] = run;
+                wb[v * R + d] = run;
+                run += c;
+            }
+            L.cnt[d] = run;
+        }
+        __syncthreads();
+        uint64_t* st = a.state + (int64_t)tile * S;
+        for (int32_t s = tid; s < S; s += T_) {
+            const int32_t c = s < R ? L.cnt[s] : L.eh[s - R];
+            st_relaxed64(st + s, state_word(epoch, tile == 0 ? kFlagInclusive : kFlagAggregate, c));
+        }
+        // in-tile ranks now, while predecessors publish
+        tile_ranks<NW, LR>(p, ev, L.wh, lrank);
+        const int64_t tok0 = (int64_t)tile * p.tile_tokens;
+        for (int32_t s = tid; s < S; s += T_) {
+            const int32_t c = s < R ? L.cnt[s] : L.eh[s - R];
+            const int32_t excl = tile == 0 ? 0 : look_back<W>(a, tile, s, epoch, &timed_out);
+            if (tile != 0) st_relaxed64(st + s, state_word(epoch, kFlagInclusive, excl + c));
+            if (s < R) {
+                L.excl[s] = excl;
+                a.excl[(int64_t)tile * R + s] = excl;
+                if (tok0 % p.tps == 0) a.send_offset[(tok0 / p.tps) * R + s] = excl;
+                if (a.chunk_offset != nullptr && tok0 % p.tpc == 0)
+                    a.chunk_offset[(tok0 / p.tpc) * R + s] = excl;
+            }
+        }
+        __syncthreads();
+    }
+
+    // ---------------- phase B: totals, recv_offset, positions
+    for (int32_t d = tid; d < R; d += T_) L.cnt[d] = wait_total(a, d, epoch, &timed_out);
+    if (leader)
+        for (int32_t e = tid; e < E; e += T_) a.expert_count[e] = wait_total(a, R + e, epoch, &timed_out);
+    __syncthreads();
+    {   // exclusive scan of the rank totals; thread i owns a run of ranks
+        const int per = (R + T_ - 1) / T_;
+        int32_t mine = 0;
+        for (int i = 0; i < per; ++i) {
+            const int32_t d = tid * per + i;
+            if (d < R) mine += L.cnt[d];
+        }
+        const int lane = tid & 63, w = tid >> 6;
+        int32_t inc = mine;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int32_t u = __shfl_up(inc, o, 64);
+            if (lane >= o) inc += u;
+        }
+        if (lane == 63) L.tmp[w] = inc;
+        __syncthreads();
+        int32_t run = inc - mine;
+        for (int i = 0; i < w; ++i) run += L.tmp[i];
+        for (int i = 0; i < per; ++i) {
+            const int32_t d = tid * per + i;
+            if (d < R) {
+                L.off[d] = run;
+                run += L.cnt[d];
+            }
+        }
+    }
+    __syncthreads();
+    if (leader) {
+        for (int32_t d = tid; d < R; d += T_) {
+            a.rank_count[d] = L.cnt[d];
+            a.recv_offset[d] = L.off[d];
+        }
+        if (tid == 0) a.recv_offset[R] = L.off[R - 1] + L.cnt[R - 1];
+    }
+    for (uint32_t m = 0; m < n_mine; ++m) {
+        const int64_t tile = L.tiles[m];
+        int32_t q[LR];
+        if (m + 1 == n_mine) {     // the last claimed tile: ids and in-tile ranks in registers
+#pragma unroll
+            for (int i = 0; i < LR; ++i) {
+                const uint32_t d = rank_of((uint32_t)ev[i], p.epr_magic);
+                q[i] = L.off[d] + L.excl[d] + lrank[i];
+            }
+        } else {                   // an earlier tile of this workgroup: rebuild from its state
+            int32_t ids[LR];
+            load_ids<NW, LR>(a, tile, ids);
+            bool ignore = false;
+            check_ids<NW, LR>(p, ids, &ignore);
+            __syncthreads();
+            for (int i = tid; i < NW * R; i += T_) {
+                const int32_t d = i % R;
+                L.wh[i] = L.off[d] + a.excl[tile * R + d] + a.wbase[tile * NW * R + i];
+            }
+            __syncthreads();
+            tile_ranks<NW, LR>(p, ids, L.wh, q);
+        }
+        store_positions<NW, LR, COH_POS>(a, tile, q, &bad_pos);
+    }
+
+    if (bad) raise_status(&a.hdr[kHdrStatus], UBEP_ERR_BAD_EXPERT_ID);
+    if (timed_out) raise_status(&a.hdr[kHdrStatus], UBEP_ERR_TIMEOUT);
+    if (bad_pos) raise_status(&a.hdr[kHdrStatus], UBEP_ERR_BAD_POSITION);
+}
+
+// The last workgroup out of a kernel that ran layout workers resets the
+// tickets and counters and advances the epoch.  Every workgroup's final
+// ticket claim returned before its increment here.
+__device__ __forceinline__ void layout_finish(const LayoutArgs& a, uint32_t epoch) {
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const uint32_t done = add_relaxed(&a.hdr[kHdrLayoutDone], 1u);
+        if (done == gridDim.x - 1u) {
+            st_relaxed(&a.hdr[kHdrLayoutTicket], 0u);
+            st_relaxed(&a.hdr[kHdrRoleTicket], 0u);
+            st_relaxed(&a.hdr[kHdrPosReady], 0u);
+            st_relaxed(&a.hdr[kHdrLayoutDone], 0u);
+            st_relaxed(&a.hdr[kHdrLayoutEpoch], epoch + 1u);
+        }
+    }
+}
+
+}  // namespace ubep

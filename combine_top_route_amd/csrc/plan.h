@@ -27,6 +27,8 @@ constexpr int kHdrFusedTicket = 64;    // task ticket of the chunk pipeline
 constexpr int kHdrFusedDone = 96;      // workgroups finished in the chunk pipeline
 constexpr int kHdrLayoutDone = 128;    // workgroups finished in the layout
 constexpr int kHdrLayoutEpoch = 160;   // layout calls completed (tags look-back state)
+constexpr int kHdrRoleTicket = 192;    // role ticket of the fused layout + dispatch kernel
+constexpr int kHdrPosReady = 224;      // layout workers whose positions are stored
 constexpr size_t kHdrBytes = 1024;
 constexpr int kFlagStride = 32;        // uint32 per chunk ready flag (128 bytes)
 
@@ -39,7 +41,6 @@ constexpr uint32_t kFlagAggregate = 1u << 30;   // this tile's own count is know
 constexpr uint32_t kFlagInclusive = 2u << 30;   // count of this and all earlier tiles
 constexpr int kLookbackWindow = 32;              // predecessor states read per round
 constexpr int kMaxTilesPerGroup = 256;           // tiles one layout workgroup may claim
-constexpr int kRowsPerLane = (int)(kTileRowsMax / kLayoutWaves / 64);  // ids a lane holds
 constexpr int64_t kMaxStateWords = (int64_t)1 << 26;                   // look-back state cap
 
 struct Plan {

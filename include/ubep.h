@@ -117,12 +117,25 @@ ubep_status ubep_workspace_init(void *ws, size_t ws_bytes, hipStream_t stream);
  *   recv_src[T*k]      inverse of pos: recv_src[pos[t][j]] = t*k + j (may be NULL).
  * A topk_idx entry outside [0, E) sets UBEP_ERR_BAD_EXPERT_ID in the device
  * status; the outputs are then unspecified but every pos stays in [0, T*k).
- * Two kernels on `stream`: tile histograms with a decoupled look-back scan,
- * then stable in-tile ranking. */
+ * One kernel on `stream` (a persistent decoupled look-back over tiles of
+ * whole tokens; a one-workgroup kernel for problems of at most 4096 rows). */
 ubep_status ubep_layout(const ubep_shape *shape /*host*/, const int32_t *topk_idx,
                         int32_t *pos, int32_t *expert_count, int32_t *rank_count,
                         int32_t *recv_offset, int32_t *send_offset, int32_t *chunk_offset,
                         int32_t *recv_src, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Layout and bf16 dispatch in one launch ("Kernel Decomposition": a few
+ * workgroups compute the layout and publish it to global memory while the
+ * others load their token rows and poll for it, instead of a barrier between
+ * the two stages).  Outputs and errors are exactly those of ubep_layout
+ * followed by ubep_dispatch(UBEP_BF16) on the same stream; the caller's pos is
+ * both an output and the dispatch's input.  Shapes whose layout needs more
+ * than 24 KB of LDS per workgroup run as those two launches. */
+ubep_status ubep_layout_dispatch(const ubep_shape *shape /*host*/, const int32_t *topk_idx,
+                                 const void *x, int32_t *pos, int32_t *expert_count,
+                                 int32_t *rank_count, int32_t *recv_offset, int32_t *send_offset,
+                                 int32_t *chunk_offset, int32_t *recv_src, void *recv, void *ws,
+                                 size_t ws_bytes, hipStream_t stream);
 
 /* Dispatch ("send tokens" + "reorder tokens", written straight into the final
  * receive row: no relay buffer).  For every (t, j):

@@ -168,3 +168,23 @@ def test_invalid_arguments_rejected_before_launch():
         ubep.ubep_dispatch_combine_chunked(dict(T=8, H=64, E=4, k=2, R=2, C=2), b.x, b.pos,
                                            b.topk_w, b.recv, b.out, [0, 0], b.ws)
     assert e.value.code == ubep.ERR_INVALID_ARG
+
+
+def test_fused_and_separate_calls_share_a_workspace():
+    """Layout epochs and tickets hand over between the fused launch, the
+    separate layout, and the chunk pipeline on one workspace."""
+    w = custom(T=1024, H=512, E=64, k=8, R=16, C=4, routing="zipf", seed=12)
+    s = w.shape
+    L = oracle.layout(w.topk_idx, s.E, s.R, s.C)
+    y = oracle.dispatch_bf16(w.x, L["pos"])
+    out = oracle.combine(y, L["pos"], w.topk_w)
+    b = upload(w)
+    for mode in ("fused", "separate", "fused", "chunked", "fused", "fused"):
+        say(f"shared workspace: {mode}")
+        b.out.zero_()
+        run_path(b, fused=mode == "fused", chunked=mode == "chunked")
+        torch.cuda.synchronize()
+        assert device_status(b) == ubep.OK, mode
+        np.testing.assert_array_equal(to_np(b.pos), L["pos"])
+        np.testing.assert_array_equal(to_np(b.recv), y)
+        np.testing.assert_array_equal(to_np(b.out), out)

@@ -42,11 +42,11 @@ def _small_workload(spec, payload="bf16"):
     return custom(weights="softmax", payload=payload, **spec)
 
 
-def _full_compare(w):
+def _full_compare(w, fused=False):
     s = w.shape
-    say(f"full compare {w.recipe.note or s}")
+    say(f"full compare {w.recipe.note or s} fused={fused}")
     b = upload(w)
-    run_path(b)
+    run_path(b, fused=fused)
     torch.cuda.synchronize()
     assert device_status(b) == ubep.OK
     L = oracle_layout(w)
@@ -72,9 +72,11 @@ def test_small_configs_bit_exact(name):
     _full_compare(workload(name))
 
 
+@pytest.mark.parametrize("fused", [False, True], ids=["separate", "fused"])
 @pytest.mark.parametrize("spec", MEDIUM, ids=lambda s: f"T{s['T']}H{s['H']}E{s['E']}k{s['k']}R{s['R']}C{s['C']}")
-def test_medium_shapes_bit_exact(spec):
-    _full_compare(_small_workload(spec))
+def test_medium_shapes_bit_exact(spec, fused):
+    """fused: ubep_layout_dispatch (layout workers and data workers in one launch)."""
+    _full_compare(_small_workload(spec), fused=fused)
 
 
 @pytest.mark.parametrize("spec", [dict(T=256, H=512, E=16, k=4, R=4, C=2, routing="zipf", seed=8),
@@ -93,12 +95,12 @@ def test_full_size_layout_bit_exact(name):
     assert_layout_equal(got, oracle_layout(w), w.shape.C)
 
 
-def _check_full_path(name, chunked=False, order=None, n_sample=48):
+def _check_full_path(name, chunked=False, order=None, n_sample=48, fused=False):
     w = workload(name)
     s = w.shape
-    say(f"full path {name} chunked={chunked} order={order}")
+    say(f"full path {name} chunked={chunked} order={order} fused={fused}")
     b = upload(w)
-    run_path(b, chunked=chunked, chunk_order=order)
+    run_path(b, chunked=chunked, chunk_order=order, fused=fused)
     torch.cuda.synchronize()
     assert device_status(b) == ubep.OK
     L = oracle_layout(w)
@@ -141,6 +143,11 @@ def _check_full_path(name, chunked=False, order=None, n_sample=48):
 @pytest.mark.parametrize("name", FULL[:3])
 def test_full_size_path_sampled(name):
     _check_full_path(name)
+
+
+@pytest.mark.parametrize("name", FULL[:2])
+def test_full_size_fused_layout_dispatch_sampled(name):
+    _check_full_path(name, fused=True)
 
 
 def test_large_prefill_chunked_sampled():
