@@ -66,6 +66,7 @@ def lib() -> C.CDLL:
             "ubep_get_device_status": ([P, SZ, P, C.POINTER(C.c_int)], C.c_int),
             "ubep_identity_expert_fp8": ([I64, I64, P, P, P, P], C.c_int),
             "ubep_copy": ([P, P, SZ, P], C.c_int),
+            "ubep_set_layout_workers": ([I32], C.c_int),
         }
         for name, (args, res) in sig.items():
             f = getattr(L, name)
@@ -188,3 +189,7 @@ def ubep_identity_expert_fp8(rows, H, q, scale, y, stream=None):
 
 def ubep_copy(src, dst, nbytes, stream=None):
     _check(lib().ubep_copy(_ptr(src), _ptr(dst), nbytes, _stream(stream)), "ubep_copy")
+
+
+def ubep_set_layout_workers(n: int):
+    _check(lib().ubep_set_layout_workers(int(n)), "ubep_set_layout_workers")

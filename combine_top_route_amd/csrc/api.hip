@@ -57,6 +57,7 @@ void make_plan(const ubep_shape& s, Plan* p) {
     p->dbits = bits_for(s.R);
     p->ebits = bits_for(s.E);
     p->slots = s.R + s.E;
+    p->gather = (p->n_tiles * s.R <= kGatherMaxWords && p->n_tiles <= kGatherMaxTiles) ? 1 : 0;
     size_t off = align_up(kHdrBytes, 256);
     p->off_state = off;
     off = align_up(off + (size_t)p->n_tiles * p->slots * 8, 256);
@@ -271,6 +272,12 @@ ubep_status ubep_copy(const void* src, void* dst, size_t bytes, hipStream_t stre
         return UBEP_ERR_INVALID_ARG;
     if (bytes == 0) return UBEP_OK;
     return hip_status(launch_copy(src, dst, bytes, stream));
+}
+
+ubep_status ubep_set_layout_workers(int32_t n) {
+    if (n < 0) return UBEP_ERR_INVALID_ARG;
+    set_layout_worker_cap(n);
+    return UBEP_OK;
 }
 
 }  // extern "C"

@@ -123,8 +123,8 @@ __global__ __launch_bounds__(kChunkBlock) void chunked_kernel(ChunkArgs a) {
             }
             __syncthreads();
             for (int64_t t = t_lo + tid / G; t < t_hi; t += TPB)
-                combine_row<G, VPT, 8, true>(a.recv, a.pos, a.w, a.out, t, a.k, a.nvec, a.n_rows,
-                                             gtid, status);
+                combine_row<G, VPT, 8, true, false>(a.recv, a.pos, a.w, a.out, t, a.k, a.nvec,
+                                                    a.n_rows, gtid, status);
         }
     }
 

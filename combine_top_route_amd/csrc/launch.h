@@ -15,6 +15,7 @@ hipError_t launch_layout(const Plan& p, const int32_t* idx, int32_t* pos, int32_
                          hipStream_t stream);
 
 int64_t layout_workers(const Plan& p, int cus);
+void set_layout_worker_cap(int32_t n);   // 0: default
 
 hipError_t launch_layout_dispatch(const Plan& p, const int32_t* idx, const void* x, int32_t* pos,
                                   int32_t* expert_count, int32_t* rank_count, int32_t* recv_offset,

@@ -12,6 +12,8 @@
 // LDS.  With no value crossing workgroups it avoids the device-memory round
 // trips (ticket, publish, look-back, totals) that bound the persistent
 // kernel's latency.
+#include <atomic>
+
 #include "launch.h"
 #include "layout_worker.h"
 
@@ -178,11 +180,19 @@ __global__ __launch_bounds__(kSingleThreads) void layout_single_kernel(LayoutArg
     if (bad_pos) raise_status(&a.hdr[kHdrStatus], UBEP_ERR_BAD_POSITION);
 }
 
-// Workers of the persistent layout: enough to fill the chip, never more than
-// tiles, and few enough tiles per worker for its LDS tile list.
+static std::atomic<int32_t> g_worker_cap{0};
+
+void set_layout_worker_cap(int32_t n) { g_worker_cap.store(n, std::memory_order_relaxed); }
+
+// Workers of the persistent layout: enough to fill the chip (or the cap set
+// by ubep_set_layout_workers), never more than tiles, and few enough tiles
+// per worker for its claim limit.
 int64_t layout_workers(const Plan& p, int cus) {
     int64_t n = 2 * (int64_t)cus;
-    const int64_t need = (p.n_tiles + kMaxTilesPerGroup - 1) / kMaxTilesPerGroup;
+    const int32_t user = g_worker_cap.load(std::memory_order_relaxed);
+    if (user > 0 && user < n) n = user;
+    const int64_t cap = layout_claim_limit(p);
+    const int64_t need = (p.n_tiles + cap - 1) / cap;
     if (n < need) n = need;
     if (n > p.n_tiles) n = p.n_tiles;
     return n;

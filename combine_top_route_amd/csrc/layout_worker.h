@@ -9,22 +9,30 @@
 // of whole tokens; a tile never straddles a source-rank or chunk boundary.
 // Each tile has R + E "digits": one per destination rank, one per expert.
 //
-// Phase A -- the worker takes tiles from a ticket counter, in order:
+// Phase A -- the worker takes tiles from a ticket counter, in order, and
+//   claims its next tile while it works on the current one:
 //   * each wave loads all of its ids in one burst, then counts per-wave rank
 //     histograms and the tile's expert histogram with LDS atomics;
-//   * publishes the tile's per-digit aggregate, computes the in-tile stable
-//     ranks (ballot peer masks per 64-row step, per-wave bases across waves)
-//     while predecessors publish, then looks back over earlier tiles'
-//     published words, 32 predecessors per round (decoupled look-back), and
-//     publishes the inclusive count.  Tiles are handed out in order, so every
-//     awaited tile is held by a running workgroup that publishes its
-//     aggregate without waiting: no grid barrier, no co-residency assumption;
-//   * a tile's exclusive prefix at a source-rank / chunk boundary is a row of
+//   * publishes the tile's per-digit aggregate and computes the in-tile
+//     stable ranks (ballot peer masks per 64-row step, per-wave bases across
+//     waves);
+//   * look-back mode only: looks back over earlier tiles' published words,
+//     32 predecessors per round (decoupled look-back), and publishes the
+//     inclusive count.  Tiles are handed out in order, so every awaited tile
+//     is held by a running workgroup that publishes its aggregate without
+//     waiting: no grid barrier, no co-residency assumption.  A tile's
+//     exclusive prefix at a source-rank / chunk boundary is a row of
 //     send_offset / chunk_offset.
-// Phase B -- after the ticket counter runs dry, the worker waits for the last
-//   tile's inclusive words (the totals; everything awaited is already
-//   claimed), scans the rank totals into recv_offset and writes pos /
-//   recv_src for its tiles.  Workgroup 0 of the workers writes the totals.
+// Phase B -- after the ticket counter runs dry (so every tile is held by a
+//   running workgroup whose phase A does not wait on this one):
+//   * look-back mode: the worker waits for the last tile's inclusive words
+//     (the totals);
+//   * gather mode (few tiles): the worker reads every tile's rank aggregates
+//     once, which gives both its own tiles' exclusive prefixes and the
+//     totals in a single round of loads, and sums one slice of the expert
+//     aggregates into expert_count;
+//   then it scans the rank totals into recv_offset and writes pos / recv_src
+//   for its tiles.  Workgroup 0 of the workers writes the rank totals.
 // Words of an older epoch read as "not yet published", so nothing is cleared
 // between calls; the kernel's last workgroup resets the tickets and advances
 // the epoch.
@@ -61,10 +69,17 @@ struct LayoutLds {
     uint32_t* tiles;  // [kMaxTilesPerGroup] tiles this workgroup claimed
     int32_t* tmp;     // [NW]
     uint32_t* ticket; // [1]
+    int32_t* bins;    // gather mode: [kGatherMaxMine + 1][R] rank counts binned by own tiles
 };
 
+// Tiles one worker may claim.
+__host__ __device__ inline int64_t layout_claim_limit(const Plan& p) {
+    return p.gather ? kGatherMaxMine : kMaxTilesPerGroup;
+}
+
 inline int64_t layout_lds_bytes(const Plan& p, int nw) {
-    return 4 * ((int64_t)nw * p.R + p.E + 3 * (int64_t)p.R + kMaxTilesPerGroup + nw + 1);
+    const int64_t bins = p.gather ? (int64_t)(kGatherMaxMine + 1) * p.R : 0;
+    return 4 * ((int64_t)nw * p.R + p.E + 3 * (int64_t)p.R + kMaxTilesPerGroup + nw + 1 + bins);
 }
 
 __device__ __forceinline__ LayoutLds carve_lds(int32_t* base, const Plan& p, int nw) {
@@ -77,6 +92,7 @@ __device__ __forceinline__ LayoutLds carve_lds(int32_t* base, const Plan& p, int
     L.tiles = reinterpret_cast<uint32_t*>(L.off + p.R);
     L.tmp = reinterpret_cast<int32_t*>(L.tiles + kMaxTilesPerGroup);
     L.ticket = reinterpret_cast<uint32_t*>(L.tmp + nw);
+    L.bins = reinterpret_cast<int32_t*>(L.ticket + 1);
     return L;
 }
 
@@ -267,6 +283,59 @@ __device__ __forceinline__ int32_t wait_total(const LayoutArgs& a, int32_t slot,
     }
 }
 
+// Count of a published state word; spins on the word until its tile has
+// published in this epoch (bounded by spin_ticks).
+__device__ __forceinline__ int32_t settle(const uint64_t* w, uint64_t v, uint32_t epoch,
+                                          uint64_t spin_ticks, bool* timed_out) {
+    const auto published = [epoch](uint64_t x) {
+        return (uint32_t)(x >> 32) == epoch && ((uint32_t)x & ~kCountMask) != 0u;
+    };
+    if (!published(v)) {
+        const uint64_t t0 = now_ticks();
+        for (;;) {
+            __builtin_amdgcn_s_sleep(1);
+            v = ld_relaxed64(w);
+            if (published(v)) break;
+            if (now_ticks() - t0 > spin_ticks) {
+                *timed_out = true;
+                return 0;
+            }
+        }
+    }
+    return (int32_t)((uint32_t)v & kCountMask);
+}
+
+// Gather mode: the aggregates of `n_cols` digits starting at `col0` for every
+// tile, pair q = tile * n_cols + column, kGatherBurst loads in flight per
+// thread (clamped to the first pair past the end, so all are valid), each
+// passed to f(tile, column, count) once published.
+template <int NT, typename F>
+__device__ __forceinline__ void gather_aggregates(const LayoutArgs& a, int32_t col0, int32_t n_cols,
+                                                  uint32_t epoch, bool* timed_out, F&& f) {
+    const int32_t S = a.p.slots;
+    const int32_t n = (int32_t)a.p.n_tiles * n_cols;
+    for (int32_t q0 = 0; q0 < n; q0 += NT * kGatherBurst) {
+        uint64_t v[kGatherBurst];
+        const uint64_t* w[kGatherBurst];
+#pragma unroll
+        for (int u = 0; u < kGatherBurst; ++u) {
+            const int32_t q_raw = q0 + u * NT + (int32_t)threadIdx.x;
+            const int32_t q = q_raw < n ? q_raw : 0;
+            const int32_t j = q / n_cols, c = q - j * n_cols;
+            w[u] = a.state + (int64_t)j * S + col0 + c;
+            v[u] = ld_relaxed64(w[u]);
+        }
+#pragma unroll
+        for (int u = 0; u < kGatherBurst; ++u) {
+            const int32_t q = q0 + u * NT + (int32_t)threadIdx.x;
+            if (q < n) {
+                const int32_t j = q / n_cols, c = q - j * n_cols;
+                f(j, c, settle(w[u], v[u], epoch, a.spin_ticks, timed_out));
+            }
+        }
+    }
+}
+
 // One worker workgroup (worker `wid` of `nw_workers`): phases A and B for
 // the tiles it claims.  Worker 0 writes the totals.  Returns once this
 // workgroup's pos / recv_src are stored (COH_POS: with device-coherent stores).
@@ -283,23 +352,28 @@ __device__ __forceinline__ void layout_worker(const LayoutArgs& a, const LayoutL
     int32_t ev[LR];                                  // ids of the last claimed tile
     int32_t lrank[LR];                               // their ranks inside the tile
 
-    // ---------------- phase A: counts, in-tile ranks and look-back, tile by tile
-    // (the launch guarantees workers * kMaxTilesPerGroup >= n_tiles; a full
-    // tile list stops claiming)
+    // ---------------- phase A: counts, in-tile ranks (and look-back), tile by tile
+    // (the launch guarantees workers * claim limit >= n_tiles; at its limit a
+    // worker stops claiming)
+    const bool gather = p.gather != 0;
+    const uint32_t cap = (uint32_t)layout_claim_limit(p);
+    uint32_t claim = 0;                              // thread 0: the claim in flight
+    if (tid == 0) claim = add_relaxed(&a.hdr[kHdrLayoutTicket], 1u);
+    // the first ticket is usually the worker's own index: fetch that tile's
+    // ids while the claim is in flight, refetch below if it is another
+    int32_t nv[LR];
+    if (wid < (uint64_t)p.n_tiles) load_ids<NW, LR>(a, wid, nv);
     for (;;) {
-        if (n_mine >= (uint32_t)kMaxTilesPerGroup) break;
-        if (tid == 0) *L.ticket = add_relaxed(&a.hdr[kHdrLayoutTicket], 1u);
-        // the ticket is usually this guess: fetch that tile's ids while the
-        // ticket is in flight, refetch below if the guess was wrong
-        const uint32_t guess = wid + n_mine * nw_workers;
-        int32_t nv[LR];
-        if (guess < (uint64_t)p.n_tiles) load_ids<NW, LR>(a, guess, nv);
+        if (tid == 0) *L.ticket = claim;
         for (int i = tid; i < NW * R; i += T_) L.wh[i] = 0;
         for (int i = tid; i < E; i += T_) L.eh[i] = 0;
         __syncthreads();
         const uint32_t tile = *L.ticket;
         if (tile >= (uint64_t)p.n_tiles) break;
-        if (tile != guess) load_ids<NW, LR>(a, tile, nv);
+        if (n_mine > 0 || tile != wid) load_ids<NW, LR>(a, tile, nv);
+        // claim the next tile now, so the claim's round trip overlaps this
+        // tile's work; at the claim limit claim nothing and stop after it
+        if (tid == 0) claim = n_mine + 1 < cap ? add_relaxed(&a.hdr[kHdrLayoutTicket], 1u) : 0xFFFFFFFFu;
 #pragma unroll
         for (int i = 0; i < LR; ++i) ev[i] = nv[i];
         check_ids<NW, LR>(p, ev, &bad);
@@ -327,28 +401,68 @@ __device__ __forceinline__ void layout_worker(const LayoutArgs& a, const LayoutL
             const int32_t c = s < R ? L.cnt[s] : L.eh[s - R];
             st_relaxed64(st + s, state_word(epoch, tile == 0 ? kFlagInclusive : kFlagAggregate, c));
         }
-        // in-tile ranks now, while predecessors publish
+        // in-tile ranks now, while the other tiles publish
         tile_ranks<NW, LR>(p, ev, L.wh, lrank);
-        const int64_t tok0 = (int64_t)tile * p.tile_tokens;
-        for (int32_t s = tid; s < S; s += T_) {
-            const int32_t c = s < R ? L.cnt[s] : L.eh[s - R];
-            const int32_t excl = tile == 0 ? 0 : look_back<W>(a, tile, s, epoch, &timed_out);
-            if (tile != 0) st_relaxed64(st + s, state_word(epoch, kFlagInclusive, excl + c));
-            if (s < R) {
-                L.excl[s] = excl;
-                a.excl[(int64_t)tile * R + s] = excl;
-                if (tok0 % p.tps == 0) a.send_offset[(tok0 / p.tps) * R + s] = excl;
-                if (a.chunk_offset != nullptr && tok0 % p.tpc == 0)
-                    a.chunk_offset[(tok0 / p.tpc) * R + s] = excl;
+        if (!gather) {
+            const int64_t tok0 = (int64_t)tile * p.tile_tokens;
+            for (int32_t s = tid; s < S; s += T_) {
+                const int32_t c = s < R ? L.cnt[s] : L.eh[s - R];
+                const int32_t excl = tile == 0 ? 0 : look_back<W>(a, tile, s, epoch, &timed_out);
+                if (tile != 0) st_relaxed64(st + s, state_word(epoch, kFlagInclusive, excl + c));
+                if (s < R) {
+                    L.excl[s] = excl;
+                    a.excl[(int64_t)tile * R + s] = excl;
+                    if (tok0 % p.tps == 0) a.send_offset[(tok0 / p.tps) * R + s] = excl;
+                    if (a.chunk_offset != nullptr && tok0 % p.tpc == 0)
+                        a.chunk_offset[(tok0 / p.tpc) * R + s] = excl;
+                }
             }
         }
         __syncthreads();
     }
 
     // ---------------- phase B: totals, recv_offset, positions
-    for (int32_t d = tid; d < R; d += T_) L.cnt[d] = wait_total(a, d, epoch, &timed_out);
-    if (leader)
-        for (int32_t e = tid; e < E; e += T_) a.expert_count[e] = wait_total(a, R + e, epoch, &timed_out);
+    if (gather) {
+        // bins[b][d]: rows to rank d in the tiles j with b of this worker's
+        // tiles at or before j; so tiles[m] has the prefix bins[0..m] and the
+        // total is bins[0..n_mine]
+        const int32_t n_m = (int32_t)n_mine;
+        for (int i = tid; i < (n_m + 1) * R; i += T_) L.bins[i] = 0;
+        const int32_t e_per = (E + (int32_t)nw_workers - 1) / (int32_t)nw_workers;
+        const int32_t e_lo = (int64_t)wid * e_per < E ? (int32_t)wid * e_per : E;
+        const int32_t n_e = E - e_lo < e_per ? E - e_lo : e_per;
+        for (int i = tid; i < n_e; i += T_) L.eh[i] = 0;
+        __syncthreads();
+        gather_aggregates<T_>(a, 0, R, epoch, &timed_out, [&](int32_t j, int32_t d, int32_t c) {
+            int32_t b = 0;
+            for (int32_t m = 0; m < n_m; ++m) b += (int32_t)L.tiles[m] <= j ? 1 : 0;
+            atomicAdd(&L.bins[b * R + d], c);
+        });
+        if (n_e > 0)   // this worker's slice of the expert totals
+            gather_aggregates<T_>(a, R + e_lo, n_e, epoch, &timed_out,
+                                  [&](int32_t, int32_t e, int32_t c) { atomicAdd(&L.eh[e], c); });
+        __syncthreads();
+        for (int32_t d = tid; d < R; d += T_) {
+            int32_t run = 0;
+            for (int32_t m = 0; m < n_m; ++m) {
+                run += L.bins[m * R + d];
+                const int64_t tile = L.tiles[m];
+                const int64_t tok0 = tile * p.tile_tokens;
+                a.excl[tile * R + d] = run;
+                if (tok0 % p.tps == 0) a.send_offset[(tok0 / p.tps) * R + d] = run;
+                if (a.chunk_offset != nullptr && tok0 % p.tpc == 0)
+                    a.chunk_offset[(tok0 / p.tpc) * R + d] = run;
+                if (m + 1 == n_m) L.excl[d] = run;
+            }
+            L.cnt[d] = run + L.bins[n_m * R + d];
+        }
+        for (int i = tid; i < n_e; i += T_) a.expert_count[e_lo + i] = L.eh[i];
+    } else {
+        for (int32_t d = tid; d < R; d += T_) L.cnt[d] = wait_total(a, d, epoch, &timed_out);
+        if (leader)
+            for (int32_t e = tid; e < E; e += T_)
+                a.expert_count[e] = wait_total(a, R + e, epoch, &timed_out);
+    }
     __syncthreads();
     {   // exclusive scan of the rank totals; thread i owns a run of ranks
         const int per = (R + T_ - 1) / T_;

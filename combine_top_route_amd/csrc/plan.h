@@ -41,6 +41,12 @@ constexpr uint32_t kFlagAggregate = 1u << 30;   // this tile's own count is know
 constexpr uint32_t kFlagInclusive = 2u << 30;   // count of this and all earlier tiles
 constexpr int kLookbackWindow = 32;              // predecessor states read per round
 constexpr int kMaxTilesPerGroup = 256;           // tiles one layout workgroup may claim
+// Gather mode (few tiles): every worker sums all tiles' published counts
+// instead of looking back; a worker then claims at most kGatherMaxMine tiles.
+constexpr int64_t kGatherMaxWords = 16384;       // n_tiles * R
+constexpr int64_t kGatherMaxTiles = 512;
+constexpr int kGatherMaxMine = 8;
+constexpr int kGatherBurst = 8;                  // state words a thread loads at once
 constexpr int64_t kMaxStateWords = (int64_t)1 << 26;                   // look-back state cap
 
 struct Plan {
@@ -56,6 +62,7 @@ struct Plan {
     int64_t n_tiles;
     int32_t dbits;         // bits to hold a rank id (0..R-1)
     int32_t ebits;         // bits to hold an expert id (0..E-1)
+    int32_t gather;        // 1: prefixes and totals by gathering all tiles' counts
     // workspace byte offsets
     int32_t slots;         // look-back digits per tile: R ranks, then E experts
     size_t off_state;      // uint64 [n_tiles][R+E]  look-back state

@@ -215,13 +215,10 @@ __device__ __forceinline__ void slot_batch(const int32_t* pr, int32_t j0, int32_
     }
 }
 
-// acc[c] = fma(w_j, y[row_j][v] channel c, acc[c]) for the used slots of a batch,
-// in slot order; the KB loads are issued together.
+// The KB rows' vectors v of one batch, loaded together.
 template <int KB, bool COH>
-__device__ __forceinline__ void chain_batch(const u32x4* __restrict__ y, int64_t nvec, int64_t v,
-                                            const int64_t (&row)[KB], const bool (&use)[KB],
-                                            const float* wr, float (&acc)[8]) {
-    u32x4 r[KB];
+__device__ __forceinline__ void load_batch(const u32x4* __restrict__ y, int64_t nvec, int64_t v,
+                                           const int64_t (&row)[KB], u32x4 (&r)[KB]) {
 #pragma unroll
     for (int jj = 0; jj < KB; ++jj) {
         if constexpr (COH)
@@ -229,6 +226,13 @@ __device__ __forceinline__ void chain_batch(const u32x4* __restrict__ y, int64_t
         else
             r[jj] = __builtin_nontemporal_load(y + row[jj] * nvec + v);
     }
+}
+
+// acc[c] = fma(w_j, r_j channel c, acc[c]) for the used slots of a batch, in
+// slot order.
+template <int KB>
+__device__ __forceinline__ void fma_batch(const u32x4 (&r)[KB], const bool (&use)[KB],
+                                          const float* wr, float (&acc)[8]) {
 #pragma unroll
     for (int jj = 0; jj < KB; ++jj) {
         if (!use[jj]) continue;
@@ -241,7 +245,16 @@ __device__ __forceinline__ void chain_batch(const u32x4* __restrict__ y, int64_t
     }
 }
 
-template <int G, int VPT, int KB, bool COH = false>
+__device__ __forceinline__ u32x4 pack_bf16x8(const float (&acc)[8]) {
+    u32x4 o;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) o[c] = f32_to_bf16(acc[2 * c]) | (f32_to_bf16(acc[2 * c + 1]) << 16);
+    return o;
+}
+
+// PIPE: when k <= KB, software-pipeline the thread's vectors (KB more
+// registers of loads in flight).
+template <int G, int VPT, int KB, bool COH = false, bool PIPE = true>
 __device__ __forceinline__ void combine_row(const u32x4* __restrict__ y,
                                             const int32_t* __restrict__ pos,
                                             const float* __restrict__ w, u32x4* __restrict__ out,
@@ -256,26 +269,51 @@ __device__ __forceinline__ void combine_row(const u32x4* __restrict__ y,
     int64_t row0[KB];
     bool use0[KB];
     slot_batch<KB>(pr, 0, k, n_rows, row0, use0, &bad);
-    for (int64_t v0 = 0; v0 < nvec; v0 += (int64_t)G * VPT) {
-#pragma unroll
-        for (int i = 0; i < VPT; ++i) {
-            const int64_t v_raw = v0 + gtid + (int64_t)i * G;
-            const bool v_ok = v_raw < nvec;
-            const int64_t v = v_ok ? v_raw : 0;
-            float acc[8];
-#pragma unroll
-            for (int c = 0; c < 8; ++c) acc[c] = 0.0f;
-            chain_batch<KB, COH>(y, nvec, v, row0, use0, wr, acc);
-            for (int32_t j0 = KB; j0 < k; j0 += KB) {     // k > KB: later batches
-                int64_t row[KB];
-                bool use[KB];
-                slot_batch<KB>(pr, j0, k, n_rows, row, use, &bad);
-                chain_batch<KB, COH>(y, nvec, v, row, use, wr + j0, acc);
+    if (PIPE && k <= KB) {
+        // one batch holds every slot: software-pipeline the thread's vectors,
+        // so the next vector's KB loads are in flight while this one is reduced
+        for (int64_t v0 = 0; v0 < nvec; v0 += (int64_t)G * VPT) {
+            u32x4 r[2][KB];
+            {
+                const int64_t v_raw = v0 + gtid;
+                load_batch<KB, COH>(y, nvec, v_raw < nvec ? v_raw : 0, row0, r[0]);
             }
-            u32x4 o;
 #pragma unroll
-            for (int c = 0; c < 4; ++c) o[c] = f32_to_bf16(acc[2 * c]) | (f32_to_bf16(acc[2 * c + 1]) << 16);
-            if (v_ok) out[t * nvec + v] = o;
+            for (int i = 0; i < VPT; ++i) {
+                if (i + 1 < VPT) {
+                    const int64_t v_raw = v0 + gtid + (int64_t)(i + 1) * G;
+                    load_batch<KB, COH>(y, nvec, v_raw < nvec ? v_raw : 0, row0, r[(i + 1) & 1]);
+                }
+                float acc[8];
+#pragma unroll
+                for (int c = 0; c < 8; ++c) acc[c] = 0.0f;
+                fma_batch<KB>(r[i & 1], use0, wr, acc);
+                const int64_t v = v0 + gtid + (int64_t)i * G;
+                if (v < nvec) out[t * nvec + v] = pack_bf16x8(acc);
+            }
+        }
+    } else {
+        for (int64_t v0 = 0; v0 < nvec; v0 += (int64_t)G * VPT) {
+#pragma unroll
+            for (int i = 0; i < VPT; ++i) {
+                const int64_t v_raw = v0 + gtid + (int64_t)i * G;
+                const bool v_ok = v_raw < nvec;
+                const int64_t v = v_ok ? v_raw : 0;
+                float acc[8];
+#pragma unroll
+                for (int c = 0; c < 8; ++c) acc[c] = 0.0f;
+                u32x4 r[KB];
+                load_batch<KB, COH>(y, nvec, v, row0, r);
+                fma_batch<KB>(r, use0, wr, acc);
+                for (int32_t j0 = KB; j0 < k; j0 += KB) {     // later batches
+                    int64_t row[KB];
+                    bool use[KB];
+                    slot_batch<KB>(pr, j0, k, n_rows, row, use, &bad);
+                    load_batch<KB, COH>(y, nvec, v, row, r);
+                    fma_batch<KB>(r, use, wr + j0, acc);
+                }
+                if (v_ok) out[t * nvec + v] = pack_bf16x8(acc);
+            }
         }
     }
     if (bad && gtid == 0) raise_status(status, UBEP_ERR_BAD_POSITION);

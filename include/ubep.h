@@ -201,6 +201,14 @@ ubep_status ubep_identity_expert_fp8(int64_t rows, int64_t H, const uint8_t *q,
  * pointers); the bandwidth and counter-calibration reference. */
 ubep_status ubep_copy(const void *src, void *dst, size_t bytes, hipStream_t stream);
 
+/* Process-wide cap on the number of layout workgroups of later ubep_layout /
+ * ubep_layout_dispatch calls (n >= 1), or 0 for the default (two per compute
+ * unit, at most one per tile).  The layout still launches at least as many
+ * workgroups as its per-workgroup tile limit needs, so every result is the
+ * same; a small cap makes workgroups take several tiles (a tuning and
+ * testing control).  n < 0: UBEP_ERR_INVALID_ARG. */
+ubep_status ubep_set_layout_workers(int32_t n);
+
 #ifdef __cplusplus
 }
 #endif

@@ -47,6 +47,14 @@ def test_shape_validation():
     assert ubep.ubep_check_shape(ok, 7) == ubep.ERR_INVALID_ARG
 
 
+def test_layout_worker_cap_argument():
+    with pytest.raises(ubep.UbepError) as e:
+        ubep.ubep_set_layout_workers(-1)
+    assert e.value.code == ubep.ERR_INVALID_ARG
+    ubep.ubep_set_layout_workers(7)
+    ubep.ubep_set_layout_workers(0)
+
+
 def test_workspace_size():
     s = dict(T=4096, H=7168, E=256, k=8, R=32, C=1)
     n = ubep.ubep_workspace_bytes(s)

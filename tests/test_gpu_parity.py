@@ -79,6 +79,26 @@ def test_medium_shapes_bit_exact(spec, fused):
     _full_compare(_small_workload(spec), fused=fused)
 
 
+# worker caps that make layout workgroups take several tiles each: gather mode
+# (few tiles; 16 tiles on 2 workers is exactly the per-worker claim limit) and
+# look-back mode (256 tiles x 256 ranks)
+CAPPED = [
+    (dict(T=1024, H=64, E=64, k=8, R=16, C=4, routing="zipf", seed=21), 1),
+    (dict(T=1024, H=64, E=64, k=8, R=16, C=4, routing="zipf", seed=21), 3),
+    (dict(T=16384, H=16, E=256, k=2, R=256, C=4, routing="topk", seed=22), 5),
+]
+
+
+@pytest.mark.parametrize("fused", [False, True], ids=["separate", "fused"])
+@pytest.mark.parametrize("spec,cap", CAPPED, ids=["gather-cap1", "gather-cap3", "lookback-cap5"])
+def test_layout_workers_taking_several_tiles(spec, cap, fused):
+    ubep.ubep_set_layout_workers(cap)
+    try:
+        _full_compare(_small_workload(spec), fused=fused)
+    finally:
+        ubep.ubep_set_layout_workers(0)
+
+
 @pytest.mark.parametrize("spec", [dict(T=256, H=512, E=16, k=4, R=4, C=2, routing="zipf", seed=8),
                                   dict(T=128, H=1024, E=8, k=2, R=2, C=1, routing="topk", seed=9)])
 def test_fp8_shapes_bit_exact(spec):
