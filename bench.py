@@ -11,7 +11,10 @@ Throughput counts algorithmic bytes (what the path must read and write):
   layout   4Tk (ids) + 4Tk (positions)
   dispatch 2TH + 4Tk + 2TkH            (bf16)   |  2TH + 4Tk + TkH + 4TkH/128  (fp8)
   combine  2TkH + 8Tk + 2TH
-Time comes from HIP events on the stream the library launches on.
+Time comes from HIP events on the stream the library launches on: two at the
+ends of the timed region (marker packets between kernels would add several
+microseconds per step), and, for the dominant kernel, a pair that its own
+launch records (ubep_time_next_launch).
 
 Prints one JSON line.  Only one GPU is measured: `--gpus N` with N > 1 exits
 with a message.
@@ -78,6 +81,50 @@ def read_counters(kernel: str, workload: str):
     f_scale = copy_bytes / (float(cal["fetch_kib"]) * 1024.0)
     w_scale = copy_bytes / (float(cal["write_kib"]) * 1024.0)
     return float(got["fetch_kib"]) * 1024.0 * f_scale + float(got["write_kib"]) * 1024.0 * w_scale
+
+
+class HipEvents:
+    """Timing events made through the HIP runtime (torch's take no flags), with
+    hipEventDisableSystemFence: recording one then skips the system-scope cache
+    writeback and invalidate, which would otherwise add microseconds to every
+    timed step."""
+
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self):
+        import ctypes as C
+        self.C = C
+        self.hip = C.CDLL("libamdhip64.so.7")     # the runtime torch and libubep already share
+        self.hip.hipEventCreateWithFlags.argtypes = [C.POINTER(C.c_void_p), C.c_uint]
+        self.hip.hipEventRecord.argtypes = [C.c_void_p, C.c_void_p]
+        self.hip.hipEventElapsedTime.argtypes = [C.POINTER(C.c_float), C.c_void_p, C.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [C.c_void_p]
+        self.made = []
+
+    def pair(self):
+        out = []
+        for _ in range(2):
+            e = self.C.c_void_p()
+            if self.hip.hipEventCreateWithFlags(self.C.byref(e), self.DISABLE_SYSTEM_FENCE) != 0:
+                raise RuntimeError("hipEventCreateWithFlags failed")
+            self.made.append(e)
+            out.append(e)
+        return tuple(out)
+
+    def record(self, e, stream):
+        if self.hip.hipEventRecord(e, self.C.c_void_p(stream.cuda_stream)) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def elapsed_us(self, pair):
+        ms = self.C.c_float()
+        if self.hip.hipEventElapsedTime(self.C.byref(ms), pair[0], pair[1]) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value * 1e3
+
+    def close(self):
+        for e in self.made:
+            self.hip.hipEventDestroy(e)
+        self.made = []
 
 
 def cpu_baseline(w, reps: int) -> dict:
@@ -198,65 +245,65 @@ def main(argv=None):
         else:
             ubep.ubep_combine(sd, b.y, b.pos, b.topk_w, b.out, b.ws, stream)
 
-    def ev():
-        return torch.cuda.Event(enable_timing=True)
+    hev = HipEvents()
 
-    def step(marks):
-        """One step.  `marks` maps a point ('start', 'end', or '<call>.before' /
-        '<call>.after') to an event recorded there on the launch stream.  The
-        fp8 identity expert runs between dispatch and combine and is excluded
-        by the 'combine.before' mark."""
-        if "start" in marks:
-            marks["start"].record(stream)
+    def step(timed=None):
+        """One step.  `timed` maps a call name (or 'identity', the fp8 identity
+        expert between dispatch and combine) to a (start, stop) event pair that
+        the call's kernel launch records at its own start and end."""
         for name in calls:
-            if name + ".before" in marks:
-                marks[name + ".before"].record(stream)
+            if timed and name in timed:
+                ubep.ubep_time_next_launch(*timed[name])
             call(name)
-            if name + ".after" in marks:
-                marks[name + ".after"].record(stream)
             if name == "dispatch" and fp8:
-                if "identity.before" in marks:
-                    marks["identity.before"].record(stream)
+                if timed and "identity" in timed:
+                    ubep.ubep_time_next_launch(*timed["identity"])
                 ubep.ubep_identity_expert_fp8(s.T * s.k, s.H, b.recv, b.recv_scale, b.y, stream)
-                if "identity.after" in marks:
-                    marks["identity.after"].record(stream)
-        if "end" in marks:
-            marks["end"].record(stream)
+
+    def pairs(n):
+        return [hev.pair() for _ in range(n)]
+
+    elapsed_us = hev.elapsed_us
 
     for _ in range(args.warmup):
-        step({})
+        step()
     torch.cuda.synchronize()
     st = ubep.ubep_get_device_status(b.ws)
     if st != ubep.OK:
         print(f"device status after warm-up: {ubep.STATUS_NAMES.get(st, st)}", file=sys.stderr)
         return 1
 
-    # untimed calibration: every call bracketed, to find the dominant kernel
-    cal = []
-    for _ in range(5):
-        m = {f"{n}.{w_}": ev() for n in calls for w_ in ("before", "after")}
-        step(m)
-        cal.append(m)
+    # untimed calibration: every kernel timed by its own launch, to find the
+    # dominant one
+    cal = [{n: p for n, p in zip(calls, pairs(len(calls)))} for _ in range(5)]
     torch.cuda.synchronize()
-    per_call = {n: statistics.fmean(m[n + ".before"].elapsed_time(m[n + ".after"]) for m in cal)
-                for n in calls}
+    for c in cal:
+        step(c)
+    torch.cuda.synchronize()
+    per_call = {n: statistics.fmean(elapsed_us(c[n]) for c in cal) for n in calls}
     dom = max((n for n in calls if n != "layout"), key=lambda n: per_call[n])
 
-    # timed region: events at step start / end, around the dominant kernel, and
-    # around the fp8 identity expert (subtracted)
-    marks = []
-    for _ in range(args.steps):
-        m = {"start": ev(), "end": ev(), dom + ".before": ev(), dom + ".after": ev()}
-        if fp8:
-            m["identity.before"] = ev()
-            m["identity.after"] = ev()
-        marks.append(m)
+    # timed region: K steps between two events (per-step events only with
+    # --cold, whose cache scrub must stay outside the timing); the dominant
+    # kernel and the fp8 identity expert are timed by their own launches
+    dom_pairs = pairs(args.steps)
+    id_pairs = pairs(args.steps) if fp8 else None
+    step_pairs = pairs(args.steps) if scrub is not None else None
+    region = hev.pair()
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
+    hev.record(region[0], stream)
     for i in range(args.steps):
+        timed = {dom: dom_pairs[i]}
+        if fp8:
+            timed["identity"] = id_pairs[i]
         if scrub is not None:
             scrub.zero_()
-        step(marks[i])
+            hev.record(step_pairs[i][0], stream)
+        step(timed)
+        if scrub is not None:
+            hev.record(step_pairs[i][1], stream)
+    hev.record(region[1], stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     st = ubep.ubep_get_device_status(b.ws)
@@ -264,14 +311,15 @@ def main(argv=None):
         print(f"device status after timing: {ubep.STATUS_NAMES.get(st, st)}", file=sys.stderr)
         return 1
 
-    step_ms = []
-    for m in marks:
-        t = m["start"].elapsed_time(m["end"])
-        if fp8:
-            t -= m["identity.before"].elapsed_time(m["identity.after"])
-        step_ms.append(t)
-    dom_ms = statistics.fmean(m[dom + ".before"].elapsed_time(m[dom + ".after"]) for m in marks)
-    ms = statistics.fmean(step_ms)
+    if scrub is not None:
+        total_us = sum(elapsed_us(p_) for p_ in step_pairs)
+    else:
+        total_us = elapsed_us(region)
+    if fp8:
+        total_us -= sum(elapsed_us(p_) for p_ in id_pairs)
+    ms = total_us / args.steps / 1e3
+    dom_ms = statistics.fmean(elapsed_us(p_) for p_ in dom_pairs) / 1e3
+    hev.close()
     nb = algorithmic_bytes(sd, fp8)
     gbs = nb["total"] / (ms * 1e-3) / 1e9
     dom_bytes = nb["dispatch"] + nb["combine"] if dom == "chunked" else nb[dom]
@@ -298,9 +346,12 @@ def main(argv=None):
         "pct_of_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
         "tokens_per_s": round(s.T / (ms * 1e-3), 1),
         "bytes_per_step": nb["total"],
-        "ms": {"step_median": round(statistics.median(step_ms), 5),
-               "dominant_kernel_timed": round(dom_ms, 5),
-               "per_call_untimed_calibration": {n: round(v, 5) for n, v in per_call.items()}},
+        "ms": {"step_mean": round(ms, 5),
+               "dominant_kernel_mean": round(dom_ms, 5),
+               "per_call_calibration": {n: round(v / 1e3, 5) for n, v in per_call.items()}},
+        "timing": ("HIP events (hipEventDisableSystemFence) at the two ends of the timed "
+                   "region; the dominant kernel (and the fp8 identity expert, subtracted) "
+                   "timed by events its own launch records (hipExtLaunchKernel)"),
         "wall_ms_per_step": round(1e3 * wall / args.steps, 5),
         "rank_skew_max_over_mean": round(float(rc.max() / rc.mean()), 3),
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 2),

@@ -8,8 +8,8 @@ from ._abi import (BF16, ERR_BAD_EXPERT_ID, ERR_BAD_POSITION, ERR_HIP, ERR_INVAL
                    ERR_UNSUPPORTED, FP8_E4M3, LIB_PATH, OK, STATUS_NAMES, UbepError, lib, status_str,
                    ubep_abi_version, ubep_check_shape, ubep_combine, ubep_copy, ubep_dispatch,
                    ubep_dispatch_combine_chunked, ubep_get_device_status, ubep_identity_expert_fp8,
-                   ubep_layout, ubep_layout_dispatch, ubep_set_layout_workers, ubep_shape, ubep_workspace_bytes,
-                   ubep_workspace_init)
+                   ubep_layout, ubep_layout_dispatch, ubep_set_layout_workers, ubep_shape,
+                   ubep_time_next_launch, ubep_workspace_bytes, ubep_workspace_init)
 from .buffers import Buffers, alloc_buffers
 
 __all__ = [n for n in dir() if not n.startswith("_")]

@@ -67,6 +67,7 @@ def lib() -> C.CDLL:
             "ubep_identity_expert_fp8": ([I64, I64, P, P, P, P], C.c_int),
             "ubep_copy": ([P, P, SZ, P], C.c_int),
             "ubep_set_layout_workers": ([I32], C.c_int),
+            "ubep_time_next_launch": ([P, P], C.c_int),
         }
         for name, (args, res) in sig.items():
             f = getattr(L, name)
@@ -189,6 +190,23 @@ def ubep_identity_expert_fp8(rows, H, q, scale, y, stream=None):
 
 def ubep_copy(src, dst, nbytes, stream=None):
     _check(lib().ubep_copy(_ptr(src), _ptr(dst), nbytes, _stream(stream)), "ubep_copy")
+
+
+def ubep_time_next_launch(start, stop):
+    """start / stop: hipEvent_t handles (ctypes.c_void_p or int), torch.cuda.Event
+    objects that have been recorded once (so that they exist), or None / None
+    to clear."""
+    def handle(e):
+        if e is None:
+            return None
+        if isinstance(e, C.c_void_p):
+            h = e.value
+        else:
+            h = e.cuda_event if hasattr(e, "cuda_event") else int(e)
+        if not h:
+            raise ValueError("event not created yet: record it once first")
+        return h
+    _check(lib().ubep_time_next_launch(handle(start), handle(stop)), "ubep_time_next_launch")
 
 
 def ubep_set_layout_workers(n: int):

@@ -20,7 +20,7 @@ SOURCES = ["api.hip", "layout.hip", "layout_dispatch.hip", "dispatch.hip", "comb
            "aux.hip"]
 ARCH = os.environ.get("UBEP_OFFLOAD_ARCH", "gfx950")
 
-CFLAGS = ["-std=c++17", "-O3", "-fPIC", f"--offload-arch={ARCH}", "-ffp-contract=off",
+CFLAGS = ["-std=c++20", "-O3", "-fPIC", f"--offload-arch={ARCH}", "-ffp-contract=off",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-Wall", "-Wno-unused-function", "-I", INCLUDE, "-I", CSRC]
 

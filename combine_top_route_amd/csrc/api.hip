@@ -274,6 +274,12 @@ ubep_status ubep_copy(const void* src, void* dst, size_t bytes, hipStream_t stre
     return hip_status(launch_copy(src, dst, bytes, stream));
 }
 
+ubep_status ubep_time_next_launch(hipEvent_t start, hipEvent_t stop) {
+    if ((start == nullptr) != (stop == nullptr)) return UBEP_ERR_INVALID_ARG;
+    set_launch_events(start, stop);
+    return UBEP_OK;
+}
+
 ubep_status ubep_set_layout_workers(int32_t n) {
     if (n < 0) return UBEP_ERR_INVALID_ARG;
     set_layout_worker_cap(n);

@@ -67,9 +67,8 @@ static unsigned grid_for(int64_t items, int64_t per_block, int64_t cap) {
 hipError_t launch_identity_fp8(int64_t rows, int64_t H, const uint8_t* q, const float* scale,
                                void* y, hipStream_t stream) {
     const int64_t n = rows * (H / 16);
-    hipLaunchKernelGGL(identity_fp8_kernel, dim3(grid_for(n, 256, 65536)), dim3(256), 0, stream,
-                       reinterpret_cast<const u32x4*>(q), scale, static_cast<u32x4*>(y), rows, H);
-    return hipGetLastError();
+    return launch_kernel(identity_fp8_kernel, dim3(grid_for(n, 256, 65536)), dim3(256), 0, stream,
+                         reinterpret_cast<const u32x4*>(q), scale, static_cast<u32x4*>(y), rows, H);
 }
 
 hipError_t launch_copy(const void* src, void* dst, size_t bytes, hipStream_t stream) {
@@ -80,21 +79,28 @@ hipError_t launch_copy(const void* src, void* dst, size_t bytes, hipStream_t str
     if (e != hipSuccess) return e;
     e = device_info(dev, &di);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(copy_kernel, dim3(grid_for(n, 256 * 4, (int64_t)di.cus * 16)), dim3(256), 0,
-                       stream, static_cast<const u32x4*>(src), static_cast<u32x4*>(dst), n);
-    return hipGetLastError();
+    return launch_kernel(copy_kernel, dim3(grid_for(n, 256 * 4, (int64_t)di.cus * 16)), dim3(256), 0,
+                         stream, static_cast<const u32x4*>(src), static_cast<u32x4*>(dst), n);
 }
 
 hipError_t launch_fill_zero(void* ws, size_t bytes, hipStream_t stream) {
     const int64_t words = (int64_t)(bytes / 4);
-    hipLaunchKernelGGL(fill_zero_kernel, dim3(grid_for(words, 256, 4096)), dim3(256), 0, stream,
-                       static_cast<uint32_t*>(ws), words);
-    return hipGetLastError();
+    return launch_kernel(fill_zero_kernel, dim3(grid_for(words, 256, 4096)), dim3(256), 0, stream,
+                         static_cast<uint32_t*>(ws), words);
 }
 
 hipError_t launch_clear_status(uint32_t* status, hipStream_t stream) {
-    hipLaunchKernelGGL(clear_status_kernel, dim3(1), dim3(1), 0, stream, status);
-    return hipGetLastError();
+    return launch_kernel(clear_status_kernel, dim3(1), dim3(1), 0, stream, status);
+}
+
+static thread_local LaunchEvents g_launch_events = {nullptr, nullptr};
+
+void set_launch_events(hipEvent_t start, hipEvent_t stop) { g_launch_events = {start, stop}; }
+
+LaunchEvents take_launch_events() {
+    const LaunchEvents e = g_launch_events;
+    g_launch_events = {nullptr, nullptr};
+    return e;
 }
 
 // Immutable per-device properties, queried once per device.

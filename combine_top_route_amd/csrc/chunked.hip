@@ -186,9 +186,8 @@ hipError_t launch_chunked(const Plan& p, const void* x, const int32_t* pos, cons
         const int64_t window = grid * (int64_t)kTicketBatch;
         int64_t lag = (window + a.n - 1) / a.n;
         a.lag = (int32_t)(lag < 1 ? 1 : (lag > a.C ? a.C : lag));
-        hipLaunchKernelGGL((chunked_kernel<GG, VV>), dim3((unsigned)grid), dim3(kChunkBlock), 0,
-                           stream, a);
-        return hipGetLastError();
+        return launch_kernel(chunked_kernel<GG, VV>, dim3((unsigned)grid), dim3(kChunkBlock), 0, stream,
+                             a);
     };
     return with_group(G, VPT, go);
 }

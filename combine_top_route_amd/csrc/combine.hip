@@ -33,10 +33,9 @@ hipError_t launch_combine(const Plan& p, const void* y, const int32_t* pos, cons
     auto go = [&]<int GG, int VV>() -> hipError_t {
         constexpr int TPB = kCombineBlock / GG;
         const int64_t blocks = (p.T + TPB - 1) / TPB;
-        hipLaunchKernelGGL((combine_kernel<GG, VV>), dim3((unsigned)blocks), dim3(kCombineBlock), 0,
-                           stream, static_cast<const u32x4*>(y), pos, topk_w,
-                           static_cast<u32x4*>(out), p.T, p.k, p.H / 8, p.rows, status);
-        return hipGetLastError();
+        return launch_kernel(combine_kernel<GG, VV>, dim3((unsigned)blocks), dim3(kCombineBlock), 0,
+                             stream, static_cast<const u32x4*>(y), pos, topk_w,
+                             static_cast<u32x4*>(out), p.T, p.k, p.H / 8, p.rows, status);
     };
     return with_group(G, VPT, go);
 }

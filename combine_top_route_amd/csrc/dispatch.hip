@@ -43,10 +43,9 @@ hipError_t launch_dispatch_bf16(const Plan& p, const void* x, const int32_t* pos
     auto go = [&]<int GG, int VV>() -> hipError_t {
         constexpr int TPB = kRowBlock / GG;
         const int64_t blocks = (p.T + TPB - 1) / TPB;
-        hipLaunchKernelGGL((dispatch_bf16_kernel<GG, VV, false>), dim3((unsigned)blocks),
-                           dim3(kRowBlock), 0, stream, static_cast<const u32x4*>(x), pos,
-                           static_cast<u32x4*>(recv), p.T, p.k, p.H / 8, p.rows, status);
-        return hipGetLastError();
+        return launch_kernel(dispatch_bf16_kernel<GG, VV, false>, dim3((unsigned)blocks),
+                             dim3(kRowBlock), 0, stream, static_cast<const u32x4*>(x), pos,
+                             static_cast<u32x4*>(recv), p.T, p.k, p.H / 8, p.rows, status);
     };
     return with_group(G, VPT, go);
 }
@@ -56,10 +55,9 @@ static hipError_t launch_fp8_g(const Plan& p, const void* x, const int32_t* pos,
                                float* recv_scale, uint32_t* status, hipStream_t stream) {
     constexpr int TPB = kRowBlock / G;
     const int64_t blocks = (p.T + TPB - 1) / TPB;
-    hipLaunchKernelGGL((dispatch_fp8_kernel<G>), dim3((unsigned)blocks), dim3(kRowBlock), 0,
-                       stream, static_cast<const u32x4*>(x), pos, static_cast<u32x4*>(recv8),
-                       recv_scale, p.T, p.k, p.H, p.rows, status);
-    return hipGetLastError();
+    return launch_kernel(dispatch_fp8_kernel<G>, dim3((unsigned)blocks), dim3(kRowBlock), 0, stream,
+                         static_cast<const u32x4*>(x), pos, static_cast<u32x4*>(recv8), recv_scale,
+                         p.T, p.k, p.H, p.rows, status);
 }
 
 hipError_t launch_dispatch_fp8(const Plan& p, const void* x, const int32_t* pos, void* recv8,

@@ -2,12 +2,42 @@
 // in api.hip validates arguments and calls these.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <tuple>
 
 #include "plan.h"
 
 namespace ubep {
+
+// Events set by ubep_time_next_launch on the calling host thread: the next
+// kernel launch records them at its start and end, and clears them.
+struct LaunchEvents {
+    hipEvent_t start;
+    hipEvent_t stop;
+};
+void set_launch_events(hipEvent_t start, hipEvent_t stop);
+LaunchEvents take_launch_events();
+
+// Every library kernel launches through here: the arguments are converted to
+// the kernel's parameter types, and a pending event pair is recorded by the
+// dispatch itself (hipExtLaunchKernel), with no marker packet in the stream.
+template <typename... P, typename... A>
+hipError_t launch_kernel(void (*kernel)(P...), dim3 grid, dim3 block, size_t lds, hipStream_t stream,
+                         A... args) {
+    static_assert(sizeof...(P) == sizeof...(A), "kernel argument count");
+    std::tuple<P...> vals{static_cast<P>(args)...};
+    void* ptrs[sizeof...(P) > 0 ? sizeof...(P) : 1];
+    std::apply([&ptrs](auto&... v) {
+        int i = 0;
+        ((ptrs[i++] = static_cast<void*>(&v)), ...);
+    }, vals);
+    const LaunchEvents ev = take_launch_events();
+    return hipExtLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, ptrs, lds, stream,
+                              ev.start, ev.stop, 0);
+}
 
 hipError_t launch_layout(const Plan& p, const int32_t* idx, int32_t* pos, int32_t* expert_count,
                          int32_t* rank_count, int32_t* recv_offset, int32_t* send_offset,

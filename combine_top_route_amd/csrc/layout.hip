@@ -19,12 +19,18 @@
 
 namespace ubep {
 
+// Every workgroup is a worker and reads no header word after its last ticket
+// claim, so it counts itself done right then (the round trip overlaps phase
+// B); the last one resets.
+// LR: ids a lane holds (tiles of at most kLayoutThreads * LR rows).
+template <int LR>
 __global__ __launch_bounds__(kLayoutThreads) void layout_kernel(LayoutArgs a) {
     extern __shared__ int32_t dyn_lds[];
     const uint32_t epoch = ld_relaxed(&a.hdr[kHdrLayoutEpoch]);
     const LayoutLds L = carve_lds(dyn_lds, a.p, kLayoutWaves);
-    layout_worker<kLayoutWaves, max_lane_rows<kLayoutWaves>(), false>(a, L, epoch, blockIdx.x, gridDim.x);
-    layout_finish(a, epoch);
+    uint32_t done = 0;
+    layout_worker<kLayoutWaves, LR, false>(a, L, epoch, blockIdx.x, gridDim.x, &done);
+    if (threadIdx.x == 0 && done == gridDim.x - 1u) layout_reset(a, epoch);
 }
 
 // ---------------------------------------------------------------- one-workgroup layout
@@ -228,22 +234,27 @@ hipError_t launch_layout(const Plan& p, const int32_t* idx, int32_t* pos, int32_
         const int64_t tpw = (p.n_tiles + kSingleWaves - 1) / kSingleWaves;
         const int64_t steps = tpw * p.tile_rows / 64;
         if (steps <= 16)
-            hipLaunchKernelGGL(layout_single_kernel<16>, dim3(1), dim3(kSingleThreads), 0, stream, a);
-        else if (steps <= 32)
-            hipLaunchKernelGGL(layout_single_kernel<32>, dim3(1), dim3(kSingleThreads), 0, stream, a);
-        else
-            hipLaunchKernelGGL(layout_single_kernel<64>, dim3(1), dim3(kSingleThreads), 0, stream, a);
-        return hipGetLastError();
+            return launch_kernel(layout_single_kernel<16>, dim3(1), dim3(kSingleThreads), 0, stream, a);
+        if (steps <= 32)
+            return launch_kernel(layout_single_kernel<32>, dim3(1), dim3(kSingleThreads), 0, stream, a);
+        return launch_kernel(layout_single_kernel<64>, dim3(1), dim3(kSingleThreads), 0, stream, a);
     }
     const int64_t lds = layout_lds_bytes(p, kLayoutWaves);
-    if (lds > 64 * 1024) {
-        e = hipFuncSetAttribute(reinterpret_cast<const void*>(layout_kernel),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return e;
-    }
-    hipLaunchKernelGGL(layout_kernel, dim3((unsigned)layout_workers(p, di.cus)), dim3(kLayoutThreads),
-                       (unsigned)lds, stream, a);
-    return hipGetLastError();
+    const int64_t lane_rows = (p.tile_rows + kLayoutThreads - 1) / kLayoutThreads;
+    const auto go = [&](void (*kernel)(LayoutArgs)) -> hipError_t {
+        if (lds > 64 * 1024) {
+            const hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+            if (err != hipSuccess) return err;
+        }
+        return launch_kernel(kernel, dim3((unsigned)layout_workers(p, di.cus)), dim3(kLayoutThreads),
+                             (size_t)lds, stream, a);
+    };
+    static_assert(max_lane_rows<kLayoutWaves>() == 8, "tile rows per lane");
+    if (lane_rows <= 1) return go(layout_kernel<1>);
+    if (lane_rows <= 2) return go(layout_kernel<2>);
+    if (lane_rows <= 4) return go(layout_kernel<4>);
+    return go(layout_kernel<8>);
 }
 
 }  // namespace ubep

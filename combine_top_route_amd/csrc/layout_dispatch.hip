@@ -150,19 +150,13 @@ hipError_t launch_layout_dispatch(const Plan& p, const int32_t* idx, const void*
     auto go = [&]<int GG, int VV>() -> hipError_t {
         constexpr int TPB = kFusedThreads / GG;
         const int64_t grid = n_workers + (p.T + TPB - 1) / TPB;
-        if (lane_need <= 4)
-            hipLaunchKernelGGL((layout_dispatch_kernel<GG, VV, 4>), dim3((unsigned)grid),
-                               dim3(kFusedThreads), lds, stream, a, static_cast<const u32x4*>(x),
-                               static_cast<u32x4*>(recv), n_workers);
-        else if (lane_need <= 8)
-            hipLaunchKernelGGL((layout_dispatch_kernel<GG, VV, 8>), dim3((unsigned)grid),
-                               dim3(kFusedThreads), lds, stream, a, static_cast<const u32x4*>(x),
-                               static_cast<u32x4*>(recv), n_workers);
-        else
-            hipLaunchKernelGGL((layout_dispatch_kernel<GG, VV, 16>), dim3((unsigned)grid),
-                               dim3(kFusedThreads), lds, stream, a, static_cast<const u32x4*>(x),
-                               static_cast<u32x4*>(recv), n_workers);
-        return hipGetLastError();
+        const auto one = [&](auto kernel) {
+            return launch_kernel(kernel, dim3((unsigned)grid), dim3(kFusedThreads), lds, stream, a,
+                                 static_cast<const u32x4*>(x), static_cast<u32x4*>(recv), n_workers);
+        };
+        if (lane_need <= 4) return one(layout_dispatch_kernel<GG, VV, 4>);
+        if (lane_need <= 8) return one(layout_dispatch_kernel<GG, VV, 8>);
+        return one(layout_dispatch_kernel<GG, VV, 16>);
     };
     return with_group(G, VPT, go);
 }

@@ -339,9 +339,13 @@ __device__ __forceinline__ void gather_aggregates(const LayoutArgs& a, int32_t c
 // One worker workgroup (worker `wid` of `nw_workers`): phases A and B for
 // the tiles it claims.  Worker 0 writes the totals.  Returns once this
 // workgroup's pos / recv_src are stored (COH_POS: with device-coherent stores).
+// done (thread 0, may be null): counts the workgroup on the done counter as
+// soon as its last ticket claim has returned -- it reads no header word after
+// that -- and receives the counter's old value.
 template <int NW, int LR, bool COH_POS, int W = kLookbackWindow>
 __device__ __forceinline__ void layout_worker(const LayoutArgs& a, const LayoutLds& L, uint32_t epoch,
-                                              uint32_t wid, uint32_t nw_workers) {
+                                              uint32_t wid, uint32_t nw_workers,
+                                              uint32_t* done = nullptr) {
     const bool leader = wid == 0;
     constexpr int T_ = NW * 64;
     const Plan& p = a.p;
@@ -422,6 +426,7 @@ __device__ __forceinline__ void layout_worker(const LayoutArgs& a, const LayoutL
     }
 
     // ---------------- phase B: totals, recv_offset, positions
+    if (done != nullptr && tid == 0) *done = add_relaxed(&a.hdr[kHdrLayoutDone], 1u);
     if (gather) {
         // bins[b][d]: rows to rank d in the tiles j with b of this worker's
         // tiles at or before j; so tiles[m] has the prefix bins[0..m] and the
@@ -528,20 +533,24 @@ __device__ __forceinline__ void layout_worker(const LayoutArgs& a, const LayoutL
     if (bad_pos) raise_status(&a.hdr[kHdrStatus], UBEP_ERR_BAD_POSITION);
 }
 
-// The last workgroup out of a kernel that ran layout workers resets the
-// tickets and counters and advances the epoch.  Every workgroup's final
-// ticket claim returned before its increment here.
+// Reset the tickets and counters and advance the epoch (done by the last
+// workgroup to count itself done).
+__device__ __forceinline__ void layout_reset(const LayoutArgs& a, uint32_t epoch) {
+    st_relaxed(&a.hdr[kHdrLayoutTicket], 0u);
+    st_relaxed(&a.hdr[kHdrRoleTicket], 0u);
+    st_relaxed(&a.hdr[kHdrPosReady], 0u);
+    st_relaxed(&a.hdr[kHdrLayoutDone], 0u);
+    st_relaxed(&a.hdr[kHdrLayoutEpoch], epoch + 1u);
+}
+
+// End of a kernel that ran layout workers (and possibly workgroups that poll
+// the header until they end): the last workgroup out resets.  Every
+// workgroup's final ticket claim returned before its increment here.
 __device__ __forceinline__ void layout_finish(const LayoutArgs& a, uint32_t epoch) {
     __syncthreads();
     if (threadIdx.x == 0) {
         const uint32_t done = add_relaxed(&a.hdr[kHdrLayoutDone], 1u);
-        if (done == gridDim.x - 1u) {
-            st_relaxed(&a.hdr[kHdrLayoutTicket], 0u);
-            st_relaxed(&a.hdr[kHdrRoleTicket], 0u);
-            st_relaxed(&a.hdr[kHdrPosReady], 0u);
-            st_relaxed(&a.hdr[kHdrLayoutDone], 0u);
-            st_relaxed(&a.hdr[kHdrLayoutEpoch], epoch + 1u);
-        }
+        if (done == gridDim.x - 1u) layout_reset(a, epoch);
     }
 }
 

@@ -252,8 +252,9 @@ __device__ __forceinline__ u32x4 pack_bf16x8(const float (&acc)[8]) {
     return o;
 }
 
-// PIPE: when k <= KB, software-pipeline the thread's vectors (KB more
-// registers of loads in flight).
+// PIPE: when k <= KB, software-pipeline the thread's vectors (kPipeDepth * KB
+// more registers of loads in flight).
+constexpr int kPipeDepth = 2;
 template <int G, int VPT, int KB, bool COH = false, bool PIPE = true>
 __device__ __forceinline__ void combine_row(const u32x4* __restrict__ y,
                                             const int32_t* __restrict__ pos,
@@ -271,23 +272,26 @@ __device__ __forceinline__ void combine_row(const u32x4* __restrict__ y,
     slot_batch<KB>(pr, 0, k, n_rows, row0, use0, &bad);
     if (PIPE && k <= KB) {
         // one batch holds every slot: software-pipeline the thread's vectors,
-        // so the next vector's KB loads are in flight while this one is reduced
+        // so the loads of the next kPipeDepth vectors are in flight while
+        // this one is reduced
+        constexpr int D = kPipeDepth;
         for (int64_t v0 = 0; v0 < nvec; v0 += (int64_t)G * VPT) {
-            u32x4 r[2][KB];
-            {
-                const int64_t v_raw = v0 + gtid;
-                load_batch<KB, COH>(y, nvec, v_raw < nvec ? v_raw : 0, row0, r[0]);
+            u32x4 r[D + 1][KB];
+#pragma unroll
+            for (int i = 0; i < D && i < VPT; ++i) {
+                const int64_t v_raw = v0 + gtid + (int64_t)i * G;
+                load_batch<KB, COH>(y, nvec, v_raw < nvec ? v_raw : 0, row0, r[i]);
             }
 #pragma unroll
             for (int i = 0; i < VPT; ++i) {
-                if (i + 1 < VPT) {
-                    const int64_t v_raw = v0 + gtid + (int64_t)(i + 1) * G;
-                    load_batch<KB, COH>(y, nvec, v_raw < nvec ? v_raw : 0, row0, r[(i + 1) & 1]);
+                if (i + D < VPT) {
+                    const int64_t v_raw = v0 + gtid + (int64_t)(i + D) * G;
+                    load_batch<KB, COH>(y, nvec, v_raw < nvec ? v_raw : 0, row0, r[(i + D) % (D + 1)]);
                 }
                 float acc[8];
 #pragma unroll
                 for (int c = 0; c < 8; ++c) acc[c] = 0.0f;
-                fma_batch<KB>(r[i & 1], use0, wr, acc);
+                fma_batch<KB>(r[i % (D + 1)], use0, wr, acc);
                 const int64_t v = v0 + gtid + (int64_t)i * G;
                 if (v < nvec) out[t * nvec + v] = pack_bf16x8(acc);
             }

@@ -201,6 +201,17 @@ ubep_status ubep_identity_expert_fp8(int64_t rows, int64_t H, const uint8_t *q,
  * pointers); the bandwidth and counter-calibration reference. */
 ubep_status ubep_copy(const void *src, void *dst, size_t bytes, hipStream_t stream);
 
+/* Profiling aid: the next kernel that a ubep_* call launches from this host
+ * thread records `start` when it begins and `stop` when it ends.  The events
+ * are written by that kernel's own dispatch (hipExtLaunchKernel), so no marker
+ * packet sits between kernels; hipEventElapsedTime(start, stop) is then the
+ * kernel's duration.  Every entry point above launches one kernel, except
+ * ubep_layout_dispatch when it falls back to two launches (the first is
+ * timed).  The pair stays pending until a launch takes it, also across calls
+ * that fail validation.  Both null: clear a pending pair; exactly one null:
+ * UBEP_ERR_INVALID_ARG.  The events must have been created by the caller. */
+ubep_status ubep_time_next_launch(hipEvent_t start, hipEvent_t stop);
+
 /* Process-wide cap on the number of layout workgroups of later ubep_layout /
  * ubep_layout_dispatch calls (n >= 1), or 0 for the default (two per compute
  * unit, at most one per tile).  The layout still launches at least as many

@@ -55,6 +55,13 @@ def test_layout_worker_cap_argument():
     ubep.ubep_set_layout_workers(0)
 
 
+def test_time_next_launch_arguments():
+    with pytest.raises(ubep.UbepError) as e:       # one event of the pair missing
+        ubep.ubep_time_next_launch(1234, None)
+    assert e.value.code == ubep.ERR_INVALID_ARG
+    ubep.ubep_time_next_launch(None, None)          # clearing is always valid
+
+
 def test_workspace_size():
     s = dict(T=4096, H=7168, E=256, k=8, R=32, C=1)
     n = ubep.ubep_workspace_bytes(s)

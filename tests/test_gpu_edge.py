@@ -188,3 +188,24 @@ def test_fused_and_separate_calls_share_a_workspace():
         np.testing.assert_array_equal(to_np(b.pos), L["pos"])
         np.testing.assert_array_equal(to_np(b.recv), y)
         np.testing.assert_array_equal(to_np(b.out), out)
+
+
+def test_launch_timing_events_time_the_kernel_and_change_nothing():
+    w = custom(T=512, H=1024, E=32, k=4, R=8, seed=31)
+    s = w.shape
+    b = upload(w)
+    say("launch-recorded timing events")
+    run_path(b)
+    torch.cuda.synchronize()
+    ref = to_np(b.out).copy()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    e1.record()
+    b.out.zero_()
+    ubep.ubep_time_next_launch(e0, e1)
+    ubep.ubep_combine(s.as_dict(), b.y, b.pos, b.topk_w, b.out, b.ws)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3
+    assert 0.0 < us < 10000.0, us
+    np.testing.assert_array_equal(to_np(b.out), ref)
+    assert device_status(b) == ubep.OK
