@@ -20,8 +20,13 @@ SOURCES = ["api.hip", "layout.hip", "layout_dispatch.hip", "dispatch.hip", "comb
            "aux.hip"]
 ARCH = os.environ.get("UBEP_OFFLOAD_ARCH", "gfx950")
 
+# -amdgpu-atomic-optimizer-strategy=None: every device atomic here is issued by
+# one lane, and the optimizer's wave-level rewrite reads the result back right
+# after the atomic, which stalls the wave for a full memory round trip where
+# the code means to overlap it (ticket claims, done counts).
 CFLAGS = ["-std=c++20", "-O3", "-fPIC", f"--offload-arch={ARCH}", "-ffp-contract=off",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
           "-Wall", "-Wno-unused-function", "-I", INCLUDE, "-I", CSRC]
 
 

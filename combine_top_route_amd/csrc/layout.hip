@@ -19,9 +19,8 @@
 
 namespace ubep {
 
-// Every workgroup is a worker and reads no header word after its last ticket
-// claim, so it counts itself done right then (the round trip overlaps phase
-// B); the last one resets.
+// Every workgroup is a worker and counts itself done as soon as it has its
+// totals (the round trip overlaps the rest of phase B); the last one resets.
 // LR: ids a lane holds (tiles of at most kLayoutThreads * LR rows).
 template <int LR>
 __global__ __launch_bounds__(kLayoutThreads) void layout_kernel(LayoutArgs a) {

@@ -339,9 +339,10 @@ __device__ __forceinline__ void gather_aggregates(const LayoutArgs& a, int32_t c
 // One worker workgroup (worker `wid` of `nw_workers`): phases A and B for
 // the tiles it claims.  Worker 0 writes the totals.  Returns once this
 // workgroup's pos / recv_src are stored (COH_POS: with device-coherent stores).
-// done (thread 0, may be null): counts the workgroup on the done counter as
-// soon as its last ticket claim has returned -- it reads no header word after
-// that -- and receives the counter's old value.
+// done (thread 0, may be null): counts the workgroup on the done counter once
+// it has its totals -- its last ticket claim has returned long before, and it
+// touches no ticket, counter or epoch word after that -- and receives the
+// counter's old value (its round trip overlaps the scan and the stores).
 template <int NW, int LR, bool COH_POS, int W = kLookbackWindow>
 __device__ __forceinline__ void layout_worker(const LayoutArgs& a, const LayoutLds& L, uint32_t epoch,
                                               uint32_t wid, uint32_t nw_workers,
@@ -375,9 +376,6 @@ __device__ __forceinline__ void layout_worker(const LayoutArgs& a, const LayoutL
         const uint32_t tile = *L.ticket;
         if (tile >= (uint64_t)p.n_tiles) break;
         if (n_mine > 0 || tile != wid) load_ids<NW, LR>(a, tile, nv);
-        // claim the next tile now, so the claim's round trip overlaps this
-        // tile's work; at the claim limit claim nothing and stop after it
-        if (tid == 0) claim = n_mine + 1 < cap ? add_relaxed(&a.hdr[kHdrLayoutTicket], 1u) : 0xFFFFFFFFu;
 #pragma unroll
         for (int i = 0; i < LR; ++i) ev[i] = nv[i];
         check_ids<NW, LR>(p, ev, &bad);
@@ -385,6 +383,11 @@ __device__ __forceinline__ void layout_worker(const LayoutArgs& a, const LayoutL
         ++n_mine;
         tile_histograms<NW, LR>(p, ev, L.wh, L.eh);
         __syncthreads();
+        // claim the next tile now, after the barrier (so that the ids are in
+        // registers: a claim issued before they arrived would be waited on
+        // with them); its round trip overlaps the rest of this tile's work.
+        // At the claim limit claim nothing and stop after this tile.
+        if (tid == 0) claim = n_mine < cap ? add_relaxed(&a.hdr[kHdrLayoutTicket], 1u) : 0xFFFFFFFFu;
 
         // wave bases (kept for a later re-rank), tile aggregates, publish
         int32_t* wb = a.wbase + (int64_t)tile * NW * R;
@@ -426,16 +429,18 @@ __device__ __forceinline__ void layout_worker(const LayoutArgs& a, const LayoutL
     }
 
     // ---------------- phase B: totals, recv_offset, positions
-    if (done != nullptr && tid == 0) *done = add_relaxed(&a.hdr[kHdrLayoutDone], 1u);
+    const int32_t n_m = (int32_t)n_mine;
+    int32_t e_lo = 0, n_e = 0;      // gather mode: this worker's slice of expert_count
     if (gather) {
         // bins[b][d]: rows to rank d in the tiles j with b of this worker's
-        // tiles at or before j; so tiles[m] has the prefix bins[0..m] and the
-        // total is bins[0..n_mine]
-        const int32_t n_m = (int32_t)n_mine;
+        // tiles at or before j.  A tile j lies before tiles[m] exactly when
+        // fewer than m + 1 of them are at or before j, so the running sum
+        // over b up to m is the exclusive prefix of tiles[m], and up to
+        // n_mine the total.
         for (int i = tid; i < (n_m + 1) * R; i += T_) L.bins[i] = 0;
         const int32_t e_per = (E + (int32_t)nw_workers - 1) / (int32_t)nw_workers;
-        const int32_t e_lo = (int64_t)wid * e_per < E ? (int32_t)wid * e_per : E;
-        const int32_t n_e = E - e_lo < e_per ? E - e_lo : e_per;
+        e_lo = (int64_t)wid * e_per < E ? (int32_t)wid * e_per : E;
+        n_e = E - e_lo < e_per ? E - e_lo : e_per;
         for (int i = tid; i < n_e; i += T_) L.eh[i] = 0;
         __syncthreads();
         gather_aggregates<T_>(a, 0, R, epoch, &timed_out, [&](int32_t j, int32_t d, int32_t c) {
@@ -443,31 +448,24 @@ __device__ __forceinline__ void layout_worker(const LayoutArgs& a, const LayoutL
             for (int32_t m = 0; m < n_m; ++m) b += (int32_t)L.tiles[m] <= j ? 1 : 0;
             atomicAdd(&L.bins[b * R + d], c);
         });
-        if (n_e > 0)   // this worker's slice of the expert totals
+        if (n_e > 0)
             gather_aggregates<T_>(a, R + e_lo, n_e, epoch, &timed_out,
                                   [&](int32_t, int32_t e, int32_t c) { atomicAdd(&L.eh[e], c); });
         __syncthreads();
         for (int32_t d = tid; d < R; d += T_) {
             int32_t run = 0;
-            for (int32_t m = 0; m < n_m; ++m) {
+            for (int32_t m = 0; m <= n_m; ++m) {
                 run += L.bins[m * R + d];
-                const int64_t tile = L.tiles[m];
-                const int64_t tok0 = tile * p.tile_tokens;
-                a.excl[tile * R + d] = run;
-                if (tok0 % p.tps == 0) a.send_offset[(tok0 / p.tps) * R + d] = run;
-                if (a.chunk_offset != nullptr && tok0 % p.tpc == 0)
-                    a.chunk_offset[(tok0 / p.tpc) * R + d] = run;
-                if (m + 1 == n_m) L.excl[d] = run;
+                L.bins[m * R + d] = run;   // prefix of tiles[m] (m < n_mine), total (m = n_mine)
             }
-            L.cnt[d] = run + L.bins[n_m * R + d];
+            L.cnt[d] = run;
+            if (n_m > 0) L.excl[d] = L.bins[(n_m - 1) * R + d];
         }
-        for (int i = tid; i < n_e; i += T_) a.expert_count[e_lo + i] = L.eh[i];
     } else {
         for (int32_t d = tid; d < R; d += T_) L.cnt[d] = wait_total(a, d, epoch, &timed_out);
-        if (leader)
-            for (int32_t e = tid; e < E; e += T_)
-                a.expert_count[e] = wait_total(a, R + e, epoch, &timed_out);
     }
+    // this workgroup touches no ticket, counter or epoch word from here on
+    if (done != nullptr && tid == 0) *done = add_relaxed(&a.hdr[kHdrLayoutDone], 1u);
     __syncthreads();
     {   // exclusive scan of the rank totals; thread i owns a run of ranks
         const int per = (R + T_ - 1) / T_;
@@ -496,13 +494,6 @@ __device__ __forceinline__ void layout_worker(const LayoutArgs& a, const LayoutL
         }
     }
     __syncthreads();
-    if (leader) {
-        for (int32_t d = tid; d < R; d += T_) {
-            a.rank_count[d] = L.cnt[d];
-            a.recv_offset[d] = L.off[d];
-        }
-        if (tid == 0) a.recv_offset[R] = L.off[R - 1] + L.cnt[R - 1];
-    }
     for (uint32_t m = 0; m < n_mine; ++m) {
         const int64_t tile = L.tiles[m];
         int32_t q[LR];
@@ -520,12 +511,36 @@ __device__ __forceinline__ void layout_worker(const LayoutArgs& a, const LayoutL
             __syncthreads();
             for (int i = tid; i < NW * R; i += T_) {
                 const int32_t d = i % R;
-                L.wh[i] = L.off[d] + a.excl[tile * R + d] + a.wbase[tile * NW * R + i];
+                const int32_t excl = gather ? L.bins[m * R + d] : a.excl[tile * R + d];
+                L.wh[i] = L.off[d] + excl + a.wbase[tile * NW * R + i];
             }
             __syncthreads();
             tile_ranks<NW, LR>(p, ids, L.wh, q);
         }
         store_positions<NW, LR, COH_POS>(a, tile, q, &bad_pos);
+    }
+
+    // outputs that nothing in this kernel reads, stored last so that no wait
+    // above covers them
+    if (gather) {
+        for (int32_t d = tid; d < R; d += T_) {
+            for (int32_t m = 0; m < n_m; ++m) {
+                const int64_t tok0 = (int64_t)L.tiles[m] * p.tile_tokens;
+                if (tok0 % p.tps == 0) a.send_offset[(tok0 / p.tps) * R + d] = L.bins[m * R + d];
+                if (a.chunk_offset != nullptr && tok0 % p.tpc == 0)
+                    a.chunk_offset[(tok0 / p.tpc) * R + d] = L.bins[m * R + d];
+            }
+        }
+        for (int i = tid; i < n_e; i += T_) a.expert_count[e_lo + i] = L.eh[i];
+    } else if (leader) {
+        for (int32_t e = tid; e < E; e += T_) a.expert_count[e] = wait_total(a, R + e, epoch, &timed_out);
+    }
+    if (leader) {
+        for (int32_t d = tid; d < R; d += T_) {
+            a.rank_count[d] = L.cnt[d];
+            a.recv_offset[d] = L.off[d];
+        }
+        if (tid == 0) a.recv_offset[R] = L.off[R - 1] + L.cnt[R - 1];
     }
 
     if (bad) raise_status(&a.hdr[kHdrStatus], UBEP_ERR_BAD_EXPERT_ID);
