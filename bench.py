@@ -312,21 +312,51 @@ def main(argv=None):
         hev.record(region[1], stream)
         torch.cuda.synchronize()
         wall = time.perf_counter() - wall0
-        total_us = sum(elapsed_us(p_) for p_ in step_pairs) if cold else elapsed_us(region)
+        per_step = [elapsed_us(p_) for p_ in step_pairs] if cold else None
+        total_us = sum(per_step) if cold else elapsed_us(region)
         if fp8:
-            total_us -= sum(elapsed_us(p_) for p_ in id_pairs)
+            id_us = [elapsed_us(p_) for p_ in id_pairs]
+            total_us -= sum(id_us)
+            if cold:
+                per_step = [a_ - b_ for a_, b_ in zip(per_step, id_us)]
         return (total_us / args.steps / 1e3,
                 statistics.fmean(elapsed_us(p_) for p_ in dom_pairs) / 1e3,
-                1e3 * wall / args.steps)
+                1e3 * wall / args.steps, per_step)
+
+    def copy_ceiling(nbytes):
+        """A plain 16-byte copy moving about as many bytes as one step (half
+        read, half written; at most 2 GiB each way), in this run: the
+        achievable streaming rate that the step is compared with."""
+        n = min(nbytes // 2, 2 << 30) // 16 * 16
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        reps = 10
+        ubep.ubep_copy(src, dst, n, stream)
+        reg = hev.pair()
+        torch.cuda.synchronize()
+        hev.record(reg[0], stream)
+        for _ in range(reps):
+            ubep.ubep_copy(src, dst, n, stream)
+        hev.record(reg[1], stream)
+        torch.cuda.synchronize()
+        us = elapsed_us(reg) / reps
+        del src, dst
+        return {"bytes_moved": 2 * n, "us": round(us, 2), "GBs": round(2 * n / us / 1e3, 1)}
 
     passes = {"warm": timed_pass(False), "cold": timed_pass(True)}
+    ceiling = copy_ceiling(algorithmic_bytes(sd, fp8)["total"])
     hev.close()
     st = ubep.ubep_get_device_status(b.ws)
     if st != ubep.OK:
         print(f"device status after timing: {ubep.STATUS_NAMES.get(st, st)}", file=sys.stderr)
         return 1
     head, other = ("cold", "warm") if args.cold else ("warm", "cold")
-    ms, dom_ms, wall_ms = passes[head]
+    ms, dom_ms, wall_ms, _ = passes[head]
+    cold_steps = sorted(passes["cold"][3])
+
+    def pct(q):
+        return round(cold_steps[min(len(cold_steps) - 1, int(q * len(cold_steps)))] / 1e3, 5)
+
     nb = algorithmic_bytes(sd, fp8)
     gbs = nb["total"] / (ms * 1e-3) / 1e9
     dom_bytes = nb["dispatch"] + nb["combine"] if dom == "chunked" else nb[dom]
@@ -352,9 +382,12 @@ def main(argv=None):
                               else "warm: back-to-back steps"),
                    "seed": w.recipe.seed},
         "pct_of_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
+        "copy_ceiling": ceiling,
+        "pct_of_copy_ceiling": round(100.0 * gbs / ceiling["GBs"], 2),
         "tokens_per_s": round(s.T / (ms * 1e-3), 1),
         "bytes_per_step": nb["total"],
         "ms": {"step_mean": round(ms, 5),
+               "cold_step_p10_p50_p90": [pct(0.1), pct(0.5), pct(0.9)],
                "dominant_kernel_mean": round(dom_ms, 5),
                "per_call_calibration": {n: round(v / 1e3, 5) for n, v in per_call.items()}},
         "timing": ("HIP events (hipEventDisableSystemFence) at the two ends of the timed "
