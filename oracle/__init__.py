@@ -42,6 +42,8 @@ def lib():
         L.oracle_identity_fp8.restype = None
         L.oracle_combine.argtypes = [i64, i64, i32, p, p, p, p]
         L.oracle_combine.restype = None
+        L.oracle_gate.argtypes = [i64, i32, i32, i32, i32, C.c_int, p, p, p]
+        L.oracle_gate.restype = C.c_int
         for n in ("oracle_f32_to_e4m3_array", "oracle_f32_to_bf16_array",
                   "oracle_e4m3_to_f32_array"):
             getattr(L, n).argtypes = [i64, p, p]
@@ -162,6 +164,23 @@ def f32_to_bf16(a) -> np.ndarray:
 def bf16_to_f32(b) -> np.ndarray:
     b = np.ascontiguousarray(b, dtype=np.uint16)
     return (b.astype(np.uint32) << 16).view(np.float32)
+
+
+SOFTMAX, SIGMOID = 0, 1
+
+
+def gate(logits: np.ndarray, k: int, groups: int = 1, keep_groups: int = 1,
+         norm: int = SOFTMAX):
+    """Top-k router on fp32 logits [T, E] -> (topk_idx int32 [T, k], topk_w fp32 [T, k]).
+    Raises ValueError on arguments the definition excludes."""
+    z = np.ascontiguousarray(logits, dtype=np.float32)
+    T, E = z.shape
+    idx = np.empty((T, k), np.int32)
+    w = np.empty((T, k), np.float32)
+    st = lib().oracle_gate(T, E, k, groups, keep_groups, norm, _p(z), _p(idx), _p(w))
+    if st != OK:
+        raise ValueError(f"oracle_gate: status {st}")
+    return idx, w
 
 
 def pipeline_tokens(x, topk_idx, topk_w, E, R, C=1, payload="bf16", tokens=None):

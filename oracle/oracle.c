@@ -28,6 +28,21 @@
  *     +-448 (OCP 8-bit floating point, E4M3 "FN" flavour: bias 7, no infinity).
  * Every function here computes exactly that definition with plain loops.
  *
+ * The gate (router) step before the path follows the same pages' opening
+ * section, where each token's gate selects the experts it is sent to; the
+ * pages give no formula.  Readings taken here (oracle_gate):
+ *   - the k experts with the largest logits, larger first, equal logits in
+ *     ascending expert id;
+ *   - group-limited routing: the E experts form `groups` contiguous groups; a
+ *     group's score is its largest plus its second-largest logit (one fp32
+ *     addition; the largest alone for one-expert groups); the keep_groups
+ *     best groups (ties to the lower group id) are the only candidates;
+ *   - every selection decision is an exact fp32 comparison of logits or of
+ *     group scores;
+ *   - weights over the selected experts: softmax, exp(z_j - z_max) / sum, or
+ *     sigmoid-normalised, s(z_j) / sum s(z_i) with s(z) = 1 / (1 + exp(-z)),
+ *     evaluated in double and rounded once to fp32.
+ *
  * Parity status: every function is pinned by the CPU tests (library special
  * cases, brute force on tiny inputs, exact rational arithmetic, closed forms).
  */
@@ -276,4 +291,76 @@ void oracle_f32_to_bf16_array(int64_t n, const float *in, uint16_t *out)
 void oracle_e4m3_to_f32_array(int64_t n, const uint8_t *in, float *out)
 {
     for (int64_t i = 0; i < n; ++i) out[i] = oracle_e4m3_to_f32(in[i]);
+}
+
+/* ------------------------------------------------------------------------ */
+/* gate: logits -> top-k expert ids and normalised weights                  */
+/* ------------------------------------------------------------------------ */
+
+/* a ranks before b: larger value first, equal values in ascending id */
+static int gate_before(float va, int32_t a, float vb, int32_t b)
+{
+    return va > vb || (va == vb && a < b);
+}
+
+int oracle_gate(int64_t T, int32_t E, int32_t k, int32_t groups, int32_t keep_groups, int norm,
+                const float *logits, int32_t *topk_idx, float *topk_w)
+{
+    if (T <= 0 || E <= 0 || k <= 0 || groups <= 0 || keep_groups <= 0) return ORACLE_INVALID_ARG;
+    if (E % groups != 0 || keep_groups > groups) return ORACLE_INVALID_ARG;
+    if (norm != ORACLE_GATE_SOFTMAX && norm != ORACLE_GATE_SIGMOID) return ORACLE_INVALID_ARG;
+    const int32_t gsize = E / groups;
+    if (k > keep_groups * gsize) return ORACLE_INVALID_ARG;
+    unsigned char *allowed = malloc((size_t)E);
+    unsigned char *taken = malloc((size_t)E);
+    float *gscore = malloc(sizeof(float) * (size_t)groups);
+    unsigned char *gtaken = malloc((size_t)groups);
+    double *val = malloc(sizeof(double) * (size_t)k);
+    if (!allowed || !taken || !gscore || !gtaken || !val) {
+        free(allowed); free(taken); free(gscore); free(gtaken); free(val);
+        return ORACLE_INVALID_ARG;
+    }
+    for (int64_t t = 0; t < T; ++t) {
+        const float *z = logits + t * E;
+        /* group scores: best plus second best logit of each group */
+        for (int32_t g = 0; g < groups; ++g) {
+            int32_t b1 = -1, b2 = -1;
+            for (int32_t e = g * gsize; e < (g + 1) * gsize; ++e) {
+                if (b1 < 0 || gate_before(z[e], e, z[b1], b1)) { b2 = b1; b1 = e; }
+                else if (b2 < 0 || gate_before(z[e], e, z[b2], b2)) { b2 = e; }
+            }
+            gscore[g] = b2 < 0 ? z[b1] : z[b1] + z[b2];
+            gtaken[g] = 0;
+        }
+        /* the keep_groups best groups */
+        memset(allowed, 0, (size_t)E);
+        for (int32_t r = 0; r < keep_groups; ++r) {
+            int32_t best = -1;
+            for (int32_t g = 0; g < groups; ++g)
+                if (!gtaken[g] && (best < 0 || gate_before(gscore[g], g, gscore[best], best))) best = g;
+            gtaken[best] = 1;
+            for (int32_t e = best * gsize; e < (best + 1) * gsize; ++e) allowed[e] = 1;
+        }
+        /* the k best allowed experts, in rank order */
+        memset(taken, 0, (size_t)E);
+        for (int32_t j = 0; j < k; ++j) {
+            int32_t best = -1;
+            for (int32_t e = 0; e < E; ++e)
+                if (allowed[e] && !taken[e] && (best < 0 || gate_before(z[e], e, z[best], best)))
+                    best = e;
+            taken[best] = 1;
+            topk_idx[t * k + j] = best;
+        }
+        /* weights, in double, rounded once */
+        double sum = 0.0;
+        const double zmax = (double)z[topk_idx[t * k]];
+        for (int32_t j = 0; j < k; ++j) {
+            const double zj = (double)z[topk_idx[t * k + j]];
+            val[j] = norm == ORACLE_GATE_SOFTMAX ? exp(zj - zmax) : 1.0 / (1.0 + exp(-zj));
+            sum += val[j];
+        }
+        for (int32_t j = 0; j < k; ++j) topk_w[t * k + j] = (float)(val[j] / sum);
+    }
+    free(allowed); free(taken); free(gscore); free(gtaken); free(val);
+    return ORACLE_OK;
 }

@@ -25,5 +25,8 @@ void oracle_combine(int64_t T, int64_t H, int32_t k, const uint16_t *y, const in
 void oracle_f32_to_e4m3_array(int64_t n, const float *in, uint8_t *out);
 void oracle_f32_to_bf16_array(int64_t n, const float *in, uint16_t *out);
 void oracle_e4m3_to_f32_array(int64_t n, const uint8_t *in, float *out);
+enum { ORACLE_GATE_SOFTMAX = 0, ORACLE_GATE_SIGMOID = 1 };
+int oracle_gate(int64_t T, int32_t E, int32_t k, int32_t groups, int32_t keep_groups, int norm,
+                const float *logits, int32_t *topk_idx, float *topk_w);
 
 #endif
