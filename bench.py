@@ -11,6 +11,7 @@ Throughput counts algorithmic bytes (what the path must read and write):
   layout   4Tk (ids) + 4Tk (positions)
   dispatch 2TH + 4Tk + 2TkH            (bf16)   |  2TH + 4Tk + TkH + 4TkH/128  (fp8)
   combine  2TkH + 8Tk + 2TH
+  gate     4TE + 8Tk  (`--mode gated`: the step starts from router logits)
 Time comes from HIP events on the stream the library launches on: two at the
 ends of the timed region (marker packets between kernels would add several
 microseconds per step), and, for the dominant kernel, a pair that its own
@@ -38,16 +39,17 @@ HBM_PEAK_GBS = 8000.0
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "hbm_counters.txt")
 
 
-def algorithmic_bytes(s: dict, fp8: bool) -> dict:
+def algorithmic_bytes(s: dict, fp8: bool, gate: bool = False) -> dict:
     T, H, k = s["T"], s["H"], s["k"]
     layout = 8 * T * k
+    gate_b = 4 * T * s["E"] + 8 * T * k if gate else 0
     if fp8:
         dispatch = 2 * T * H + 4 * T * k + T * k * H + 4 * T * k * (H // 128)
     else:
         dispatch = 2 * T * H + 4 * T * k + 2 * T * k * H
     combine = 2 * T * k * H + 8 * T * k + 2 * T * H
-    return dict(layout=layout, dispatch=dispatch, combine=combine,
-                total=layout + dispatch + combine)
+    return dict(gate=gate_b, layout=layout, dispatch=dispatch, combine=combine,
+                total=gate_b + layout + dispatch + combine)
 
 
 def source_hash() -> str:
@@ -191,7 +193,8 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=None, help="workload name (default: DeepSeek-V3 decode)")
-    ap.add_argument("--mode", choices=["unfused", "chunked"], default="unfused")
+    ap.add_argument("--mode", choices=["unfused", "chunked", "gated"], default="unfused",
+                    help="gated: the step starts from router logits (ubep_gate, then unfused)")
     ap.add_argument("--cold", action="store_true",
                     help="headline the cold-cache pass (the warm one is then reported beside it)")
     ap.add_argument("--cpu-reps", type=int, default=7)
@@ -236,9 +239,20 @@ def main(argv=None):
     scrub = torch.ones(512 << 20, dtype=torch.uint8, device="cuda").view(torch.int64)
 
     calls = ["layout"] + (["chunked"] if args.mode == "chunked" else ["dispatch", "combine"])
+    gated = args.mode == "gated"
+    if gated:
+        from workloads import router_logits
+        calls = ["gate"] + calls
+        logits = torch.from_numpy(router_logits(w.recipe)).cuda()
+        grouped = w.recipe.routing == "group_zipf"
+        gate_args = dict(groups=w.recipe.n_groups if grouped else 1,
+                         keep_groups=w.recipe.topk_groups if grouped else 1,
+                         norm=ubep.GATE_SIGMOID if w.recipe.weights == "sigmoid" else ubep.GATE_SOFTMAX)
 
     def call(name):
-        if name == "layout":
+        if name == "gate":
+            ubep.ubep_gate(s.T, s.E, s.k, logits, b.topk_idx, b.topk_w, stream=stream, **gate_args)
+        elif name == "layout":
             ubep.ubep_layout(sd, b.topk_idx, b.pos, b.expert_count, b.rank_count, b.recv_offset,
                              b.send_offset, chunk_off, None, b.ws, stream)
         elif name == "chunked":
@@ -285,7 +299,7 @@ def main(argv=None):
         step(c)
     torch.cuda.synchronize()
     per_call = {n: statistics.fmean(elapsed_us(c[n]) for c in cal) for n in calls}
-    dom = max((n for n in calls if n != "layout"), key=lambda n: per_call[n])
+    dom = max((n for n in calls if n not in ("layout", "gate")), key=lambda n: per_call[n])
 
     def timed_pass(cold):
         """K steps.  Warm: back to back between two events.  Cold: a read scrub
@@ -344,7 +358,7 @@ def main(argv=None):
         return {"bytes_moved": 2 * n, "us": round(us, 2), "GBs": round(2 * n / us / 1e3, 1)}
 
     passes = {"warm": timed_pass(False), "cold": timed_pass(True)}
-    ceiling = copy_ceiling(algorithmic_bytes(sd, fp8)["total"])
+    ceiling = copy_ceiling(algorithmic_bytes(sd, fp8, gated)["total"])
     hev.close()
     st = ubep.ubep_get_device_status(b.ws)
     if st != ubep.OK:
@@ -357,7 +371,7 @@ def main(argv=None):
     def pct(q):
         return round(cold_steps[min(len(cold_steps) - 1, int(q * len(cold_steps)))] / 1e3, 5)
 
-    nb = algorithmic_bytes(sd, fp8)
+    nb = algorithmic_bytes(sd, fp8, gated)
     gbs = nb["total"] / (ms * 1e-3) / 1e9
     dom_bytes = nb["dispatch"] + nb["combine"] if dom == "chunked" else nb[dom]
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9

@@ -33,6 +33,15 @@ class ubep_shape(C.Structure):
                 ("R", C.c_int32), ("C", C.c_int32)]
 
 
+GATE_SOFTMAX = 0
+GATE_SIGMOID = 1
+
+
+class ubep_gate_shape(C.Structure):
+    _fields_ = [("T", C.c_int64), ("E", C.c_int32), ("k", C.c_int32), ("groups", C.c_int32),
+                ("keep_groups", C.c_int32), ("norm", C.c_int32)]
+
+
 class UbepError(RuntimeError):
     def __init__(self, code: int, where: str = ""):
         self.code = code
@@ -59,6 +68,7 @@ def lib() -> C.CDLL:
             "ubep_workspace_bytes": ([S], SZ),
             "ubep_workspace_init": ([P, SZ, P], C.c_int),
             "ubep_layout": ([S, P, P, P, P, P, P, P, P, P, SZ, P], C.c_int),
+            "ubep_gate": ([C.POINTER(ubep_gate_shape), P, P, P, P], C.c_int),
             "ubep_layout_dispatch": ([S, P, P, P, P, P, P, P, P, P, P, P, SZ, P], C.c_int),
             "ubep_dispatch": ([S, C.c_int, P, P, P, P, P, SZ, P], C.c_int),
             "ubep_combine": ([S, P, P, P, P, P, SZ, P], C.c_int),
@@ -131,6 +141,13 @@ def ubep_workspace_bytes(shape) -> int:
 
 def ubep_workspace_init(ws, stream=None):
     _check(lib().ubep_workspace_init(_ptr(ws), _nbytes(ws), _stream(stream)), "ubep_workspace_init")
+
+
+def ubep_gate(T, E, k, logits, topk_idx, topk_w, groups=1, keep_groups=1, norm=GATE_SOFTMAX,
+              stream=None):
+    g = ubep_gate_shape(T, E, k, groups, keep_groups, norm)
+    _check(lib().ubep_gate(C.byref(g), _ptr(logits), _ptr(topk_idx), _ptr(topk_w), _stream(stream)),
+           "ubep_gate")
 
 
 def ubep_layout(shape, topk_idx, pos, expert_count, rank_count, recv_offset, send_offset,

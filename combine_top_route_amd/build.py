@@ -16,8 +16,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libubep.so")
-SOURCES = ["api.hip", "layout.hip", "layout_dispatch.hip", "dispatch.hip", "combine.hip", "chunked.hip",
-           "aux.hip"]
+SOURCES = ["api.hip", "gate.hip", "layout.hip", "layout_dispatch.hip", "dispatch.hip", "combine.hip",
+           "chunked.hip", "aux.hip"]
 ARCH = os.environ.get("UBEP_OFFLOAD_ARCH", "gfx950")
 
 # -amdgpu-atomic-optimizer-strategy=None: every device atomic here is issued by

@@ -187,6 +187,21 @@ ubep_status ubep_layout_dispatch(const ubep_shape* s, const int32_t* topk_idx, c
                                              ws, ticks, stream));
 }
 
+ubep_status ubep_gate(const ubep_gate_shape* g, const float* logits, int32_t* topk_idx,
+                      float* topk_w, hipStream_t stream) {
+    if (g == nullptr || !logits || !topk_idx || !topk_w) return UBEP_ERR_INVALID_ARG;
+    if (g->T <= 0 || g->E <= 0 || g->k <= 0 || g->groups <= 0 || g->keep_groups <= 0)
+        return UBEP_ERR_INVALID_ARG;
+    if (g->E % g->groups != 0 || g->keep_groups > g->groups) return UBEP_ERR_INVALID_ARG;
+    if ((int64_t)g->k > (int64_t)g->keep_groups * (g->E / g->groups)) return UBEP_ERR_INVALID_ARG;
+    if (g->norm != UBEP_GATE_SOFTMAX && g->norm != UBEP_GATE_SIGMOID) return UBEP_ERR_INVALID_ARG;
+    if (g->E > kGateMaxE || g->k > kMaxK || g->groups > kGateMaxGroups) return UBEP_ERR_UNSUPPORTED;
+    if (g->T * (int64_t)g->k >= ((int64_t)1 << 31) || g->T * (int64_t)g->E >= ((int64_t)1 << 40))
+        return UBEP_ERR_UNSUPPORTED;
+    if (!aligned(logits, 4) || !aligned(topk_idx, 4) || !aligned(topk_w, 4)) return UBEP_ERR_INVALID_ARG;
+    return hip_status(launch_gate(*g, logits, topk_idx, topk_w, stream));
+}
+
 ubep_status ubep_dispatch(const ubep_shape* s, int dtype, const void* x, const int32_t* pos,
                           void* recv, float* recv_scale, void* ws, size_t ws_bytes,
                           hipStream_t stream) {

@@ -66,6 +66,9 @@ hipError_t launch_chunked(const Plan& p, const void* x, const int32_t* pos, cons
                           void* recv, void* out, const int32_t* chunk_order, uint64_t spin_ticks,
                           uint32_t debug_flags, void* ws, int device, hipStream_t stream);
 
+hipError_t launch_gate(const ubep_gate_shape& g, const float* logits, int32_t* idx, float* w,
+                       hipStream_t stream);
+
 hipError_t launch_identity_fp8(int64_t rows, int64_t H, const uint8_t* q, const float* scale,
                                void* y, hipStream_t stream);
 

@@ -13,6 +13,8 @@ constexpr int kMaxK = 32;
 constexpr int kMaxR = 1024;
 constexpr int kMaxE = 8192;
 constexpr int kMaxC = 256;
+constexpr int kGateMaxE = 1024;
+constexpr int kGateMaxGroups = 64;
 
 // Layout kernel: 8 waves per workgroup, tiles of whole tokens with at most
 // kTileRowsMax rows.

@@ -117,8 +117,10 @@ ubep_status ubep_workspace_init(void *ws, size_t ws_bytes, hipStream_t stream);
  *   recv_src[T*k]      inverse of pos: recv_src[pos[t][j]] = t*k + j (may be NULL).
  * A topk_idx entry outside [0, E) sets UBEP_ERR_BAD_EXPERT_ID in the device
  * status; the outputs are then unspecified but every pos stays in [0, T*k).
- * One kernel on `stream` (a persistent decoupled look-back over tiles of
- * whole tokens; a one-workgroup kernel for problems of at most 4096 rows). */
+ * One kernel on `stream`: persistent workgroups over tiles of whole tokens
+ * that publish per-tile counts in the workspace and read each other's (all
+ * of them at once for up to 512 tiles, a decoupled look-back beyond), or one
+ * workgroup for problems of at most 4096 rows. */
 ubep_status ubep_layout(const ubep_shape *shape /*host*/, const int32_t *topk_idx,
                         int32_t *pos, int32_t *expert_count, int32_t *rank_count,
                         int32_t *recv_offset, int32_t *send_offset, int32_t *chunk_offset,
@@ -136,6 +138,35 @@ ubep_status ubep_layout_dispatch(const ubep_shape *shape /*host*/, const int32_t
                                  int32_t *rank_count, int32_t *recv_offset, int32_t *send_offset,
                                  int32_t *chunk_offset, int32_t *recv_src, void *recv, void *ws,
                                  size_t ws_bytes, hipStream_t stream);
+
+/* ---- the gate: the routing step before the path ---- */
+
+typedef enum { UBEP_GATE_SOFTMAX = 0, UBEP_GATE_SIGMOID = 1 } ubep_gate_norm;
+
+typedef struct {
+    int64_t T;            /* tokens */
+    int32_t E;            /* experts, 1..1024 */
+    int32_t k;            /* experts per token, 1..32 */
+    int32_t groups;       /* contiguous expert groups, 1..64, dividing E (1: no groups) */
+    int32_t keep_groups;  /* groups a token may use, 1..groups; k <= keep_groups * E/groups */
+    int32_t norm;         /* ubep_gate_norm */
+} ubep_gate_shape;
+
+/* Top-k gate on router logits (opening section of the UBEP page: each token
+ * is sent to the experts its gate selects; the page gives no formula, so the
+ * rule is stated here).  logits fp32 [T][E]; outputs topk_idx int32 [T][k]
+ * and topk_w fp32 [T][k], in the layout ubep_layout reads.  Per token:
+ *   - group score = largest + second-largest logit of the group (one fp32
+ *     addition; the largest alone when groups have one expert); the
+ *     keep_groups best groups are kept, equal scores to the lower group id;
+ *   - slot j = the j-th largest logit among the kept groups' experts, equal
+ *     logits to the lower expert id (exact fp32 comparisons throughout);
+ *   - UBEP_GATE_SOFTMAX: w_j = exp(z_j - z_max) / sum over the k selected;
+ *     UBEP_GATE_SIGMOID: w_j = s(z_j) / sum s(z_i), s(z) = 1 / (1 + exp(-z));
+ *     fp32 arithmetic with expf (a few ulps from the exact value).
+ * Logits must be finite.  One kernel on `stream`, one wave per token. */
+ubep_status ubep_gate(const ubep_gate_shape *gate /*host*/, const float *logits,
+                      int32_t *topk_idx, float *topk_w, hipStream_t stream);
 
 /* Dispatch ("send tokens" + "reorder tokens", written straight into the final
  * receive row: no relay buffer).  For every (t, j):

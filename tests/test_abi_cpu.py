@@ -102,3 +102,21 @@ def test_product_path_has_no_oracle_or_fallback():
         if f.endswith(".py"):
             txt = open(os.path.join(pkg, f)).read()
             assert "import oracle" not in txt and "from oracle" not in txt, f
+
+
+def test_gate_validation_without_gpu():
+    """Invalid gate shapes return before any launch (dummy pointers are never used)."""
+    p = 256
+    cases = [dict(T=0, E=8, k=2), dict(T=4, E=8, k=9), dict(T=4, E=8, k=2, groups=3),
+             dict(T=4, E=8, k=2, groups=4, keep_groups=5), dict(T=4, E=8, k=5, groups=4, keep_groups=2),
+             dict(T=4, E=8, k=2, norm=2)]
+    for c in cases:
+        with pytest.raises(ubep.UbepError) as e:
+            ubep.ubep_gate(c["T"], c["E"], c["k"], p, p, p, c.get("groups", 1), c.get("keep_groups", 1),
+                           c.get("norm", 0), stream=0)
+        assert e.value.code == ubep.ERR_INVALID_ARG, c
+    for c in (dict(T=4, E=2048, k=2), dict(T=4, E=256, k=33), dict(T=4, E=256, k=2, groups=128)):
+        with pytest.raises(ubep.UbepError) as e:
+            ubep.ubep_gate(c["T"], c["E"], c["k"], p, p, p, c.get("groups", 1), c.get("keep_groups", 1), 0,
+                           stream=0)
+        assert e.value.code == ubep.ERR_UNSUPPORTED, c

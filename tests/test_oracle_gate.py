@@ -153,3 +153,21 @@ def test_gate_softmax_large_logits_stay_finite():
     np.testing.assert_allclose(w, _numpy_weights(z + np.float32(1000.0), idx.astype(np.int64),
                                                  oracle.SOFTMAX), rtol=0, atol=2e-7)
     np.testing.assert_allclose(w, w_ref, rtol=0, atol=2e-5)   # shift by 1000 rounds the logits
+
+
+@pytest.mark.parametrize("name", ["tiny_T128_H1024_E8_k2_R2", "dsv3_decode_T4096_H7168_E256_k8_R32",
+                                  "prefill_grouped_zipf_T65536_H7168_E256_k8_R64_C16"])
+def test_gate_reproduces_the_generators_routing(name):
+    """The workload generator selects with numpy sorts on float64 keys; the
+    oracle gate on the same keys rounded to fp32 must pick the same experts
+    (no two keys of a token are within fp32 rounding of each other here)."""
+    from workloads import CONFIGS, generate, router_logits
+    r = CONFIGS[name]
+    grouped = r.routing == "group_zipf"
+    idx, w = oracle.gate(router_logits(r), r.shape.k, r.n_groups if grouped else 1,
+                         r.topk_groups if grouped else 1,
+                         oracle.SIGMOID if r.weights == "sigmoid" else oracle.SOFTMAX)
+    ref = generate(r, tokens=1)
+    np.testing.assert_array_equal(idx, ref.topk_idx)
+    if r.routing == "topk":                     # same logits up to fp32 rounding: same weights
+        np.testing.assert_allclose(w, ref.topk_w, rtol=0, atol=1e-6)

@@ -186,6 +186,23 @@ def generate(recipe: Recipe, tokens: int | None = None) -> Workload:
                     topk_w=np.ascontiguousarray(w))
 
 
+def router_logits(recipe: Recipe) -> np.ndarray:
+    """fp32 router logits [T, E] for a gate to select from: the N(0,1) logits
+    of `topk` routing, or the Zipf selection keys (log popularity + Gumbel
+    noise) of the skewed routings.  Drawn from the same streams as generate()."""
+    s = recipe.shape
+    _, g_z, g_perm, g_gum = _streams(recipe.seed)
+    z = g_z.standard_normal(size=(s.T, s.E))
+    if recipe.routing == "topk":
+        return z.astype(np.float32)
+    logp = np.empty(s.E, dtype=np.float64)
+    perm = g_perm.permutation(s.E)
+    p = np.arange(1, s.E + 1, dtype=np.float64) ** (-recipe.zipf_s)
+    p /= p.sum()
+    logp[perm] = np.log(p)
+    return (logp[None, :] + g_gum.gumbel(size=(s.T, s.E))).astype(np.float32)
+
+
 def make_config(name: str, seed: int | None = None) -> Workload:
     r = CONFIGS[name]
     if seed is not None:
