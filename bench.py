@@ -199,6 +199,9 @@ def main(argv=None):
                     help="headline the cold-cache pass (the warm one is then reported beside it)")
     ap.add_argument("--cpu-reps", type=int, default=7)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="time replays of one step captured in a HIP graph (no host launch cost); "
+                         "the dominant kernel is still timed by its launches in eager steps")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="only run the plain 16-byte copy kernel on this many bytes (the "
                          "reference for scaling hardware traffic counters) and exit")
@@ -250,6 +253,7 @@ def main(argv=None):
                          norm=ubep.GATE_SIGMOID if w.recipe.weights == "sigmoid" else ubep.GATE_SOFTMAX)
 
     def call(name):
+        stream = torch.cuda.current_stream()    # the capture stream while a graph records
         if name == "gate":
             ubep.ubep_gate(s.T, s.E, s.k, logits, b.topk_idx, b.topk_w, stream=stream, **gate_args)
         elif name == "layout":
@@ -276,7 +280,8 @@ def main(argv=None):
             if name == "dispatch" and fp8:
                 if timed and "identity" in timed:
                     ubep.ubep_time_next_launch(*timed["identity"])
-                ubep.ubep_identity_expert_fp8(s.T * s.k, s.H, b.recv, b.recv_scale, b.y, stream)
+                ubep.ubep_identity_expert_fp8(s.T * s.k, s.H, b.recv, b.recv_scale, b.y,
+                                              torch.cuda.current_stream())
 
     def pairs(n):
         return [hev.pair() for _ in range(n)]
@@ -358,6 +363,41 @@ def main(argv=None):
         return {"bytes_moved": 2 * n, "us": round(us, 2), "GBs": round(2 * n / us / 1e3, 1)}
 
     passes = {"warm": timed_pass(False), "cold": timed_pass(True)}
+    eager = passes
+    if args.graph:
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            step()                                   # one eager step on the capture stream
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph):
+            step()
+        torch.cuda.synchronize()
+
+        def graph_pass(cold):
+            """K graph replays: warm between two events, cold with a read scrub
+            before each replay outside per-replay events."""
+            pairs_ = pairs(args.steps) if cold else None
+            region = hev.pair()
+            torch.cuda.synchronize()
+            hev.record(region[0], stream)
+            for i in range(args.steps):
+                if cold:
+                    scrub.sum()
+                    hev.record(pairs_[i][0], stream)
+                graph.replay()
+                if cold:
+                    hev.record(pairs_[i][1], stream)
+            hev.record(region[1], stream)
+            torch.cuda.synchronize()
+            per = [elapsed_us(p_) for p_ in pairs_] if cold else None
+            total = sum(per) if cold else elapsed_us(region)
+            return total / args.steps / 1e3, per
+        (gw, _), (gc, gc_steps) = graph_pass(False), graph_pass(True)
+        passes = {"warm": (gw, eager["warm"][1], eager["warm"][2], None),
+                  "cold": (gc, eager["cold"][1], eager["cold"][2], gc_steps)}
     ceiling = copy_ceiling(algorithmic_bytes(sd, fp8, gated)["total"])
     hev.close()
     st = ubep.ubep_get_device_status(b.ws)
@@ -409,6 +449,8 @@ def main(argv=None):
                    "dominant kernel (and the fp8 identity expert, subtracted) timed by "
                    "events its own launch records (hipExtLaunchKernel)"),
         "wall_ms_per_step": round(wall_ms, 5),
+        "graph": ({"eager_warm_ms_per_step": round(eager["warm"][0], 5),
+                   "eager_cold_ms_per_step": round(eager["cold"][0], 5)} if args.graph else False),
         other: {"ms_per_step": round(passes[other][0], 5),
                 "value": round(nb["total"] / (passes[other][0] * 1e-3) / 1e9, 2),
                 "pct_of_hbm_peak": round(100.0 * nb["total"] / (passes[other][0] * 1e-3) / 1e9
