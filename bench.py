@@ -193,8 +193,9 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=None, help="workload name (default: DeepSeek-V3 decode)")
-    ap.add_argument("--mode", choices=["unfused", "chunked", "gated"], default="unfused",
-                    help="gated: the step starts from router logits (ubep_gate, then unfused)")
+    ap.add_argument("--mode", choices=["unfused", "chunked", "gated", "fused"], default="unfused",
+                    help="gated: the step starts from router logits (ubep_gate, then unfused); "
+                         "fused: ubep_layout_dispatch (one launch), then combine")
     ap.add_argument("--cold", action="store_true",
                     help="headline the cold-cache pass (the warm one is then reported beside it)")
     ap.add_argument("--cpu-reps", type=int, default=7)
@@ -242,6 +243,11 @@ def main(argv=None):
     scrub = torch.ones(512 << 20, dtype=torch.uint8, device="cuda").view(torch.int64)
 
     calls = ["layout"] + (["chunked"] if args.mode == "chunked" else ["dispatch", "combine"])
+    if args.mode == "fused":
+        if fp8:
+            print("the fused launch carries a bf16 payload only", file=sys.stderr)
+            return 2
+        calls = ["layout_dispatch", "combine"]
     gated = args.mode == "gated"
     if gated:
         from workloads import router_logits
@@ -259,6 +265,10 @@ def main(argv=None):
         elif name == "layout":
             ubep.ubep_layout(sd, b.topk_idx, b.pos, b.expert_count, b.rank_count, b.recv_offset,
                              b.send_offset, chunk_off, None, b.ws, stream)
+        elif name == "layout_dispatch":
+            ubep.ubep_layout_dispatch(sd, b.topk_idx, b.x, b.pos, b.expert_count, b.rank_count,
+                                      b.recv_offset, b.send_offset, chunk_off, None, b.recv, b.ws,
+                                      stream)
         elif name == "chunked":
             ubep.ubep_dispatch_combine_chunked(sd, b.x, b.pos, b.topk_w, b.recv, b.out, None,
                                                b.ws, stream=stream)
@@ -305,6 +315,8 @@ def main(argv=None):
     torch.cuda.synchronize()
     per_call = {n: statistics.fmean(elapsed_us(c[n]) for c in cal) for n in calls}
     dom = max((n for n in calls if n not in ("layout", "gate")), key=lambda n: per_call[n])
+    if dom == "layout_dispatch":
+        dom = "combine"      # the fused launch also holds the layout's latency chain
 
     def timed_pass(cold):
         """K steps.  Warm: back to back between two events.  Cold: a read scrub
