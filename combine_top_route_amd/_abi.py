@@ -19,10 +19,11 @@ ERR_BAD_EXPERT_ID = 3
 ERR_TIMEOUT = 4
 ERR_HIP = 5
 ERR_BAD_POSITION = 6
+ERR_WORKSPACE = 7
 STATUS_NAMES = {OK: "UBEP_OK", ERR_INVALID_ARG: "UBEP_ERR_INVALID_ARG",
                 ERR_UNSUPPORTED: "UBEP_ERR_UNSUPPORTED", ERR_BAD_EXPERT_ID: "UBEP_ERR_BAD_EXPERT_ID",
                 ERR_TIMEOUT: "UBEP_ERR_TIMEOUT", ERR_HIP: "UBEP_ERR_HIP",
-                ERR_BAD_POSITION: "UBEP_ERR_BAD_POSITION"}
+                ERR_BAD_POSITION: "UBEP_ERR_BAD_POSITION", ERR_WORKSPACE: "UBEP_ERR_WORKSPACE"}
 
 BF16 = 0
 FP8_E4M3 = 1

@@ -117,6 +117,7 @@ const char* ubep_status_str(ubep_status s) {
         case UBEP_ERR_TIMEOUT: return "ready-flag wait timed out";
         case UBEP_ERR_HIP: return "HIP runtime error";
         case UBEP_ERR_BAD_POSITION: return "position outside [0, T*k)";
+        case UBEP_ERR_WORKSPACE: return "workspace counters inconsistent; re-initialize the workspace";
     }
     return "unknown status";
 }

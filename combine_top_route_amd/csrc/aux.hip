@@ -1,7 +1,11 @@
 // Auxiliary kernels, not on the dispatch/combine path: the identity expert for
 // an fp8 payload, a plain 16-byte copy (bandwidth and counter calibration),
-// workspace zero-fill and status clear.
+// workspace zero-fill and status clear; and host helpers shared by the
+// launchers (resident workgroups per kernel, pending launch events, device
+// properties).
+#include <map>
 #include <mutex>
+#include <tuple>
 
 #include "launch.h"
 #include "rows.h"
@@ -91,6 +95,34 @@ hipError_t launch_fill_zero(void* ws, size_t bytes, hipStream_t stream) {
 
 hipError_t launch_clear_status(uint32_t* status, hipStream_t stream) {
     return launch_kernel(clear_status_kernel, dim3(1), dim3(1), 0, stream, status);
+}
+
+hipError_t resident_blocks(const void* kernel, int block, size_t lds, int64_t* out) {
+    static std::mutex mu;
+    static std::map<std::tuple<int, const void*, int, size_t>, int64_t> cache;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const auto key = std::make_tuple(dev, kernel, block, lds);
+    {
+        std::lock_guard<std::mutex> lock(mu);
+        const auto it = cache.find(key);
+        if (it != cache.end()) {
+            *out = it->second;
+            return hipSuccess;
+        }
+    }
+    DeviceInfo di;
+    e = device_info(dev, &di);
+    if (e != hipSuccess) return e;
+    int per_cu = 0;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, block, lds);
+    if (e != hipSuccess) return e;
+    const int64_t n = (int64_t)(per_cu > 0 ? per_cu : 1) * di.cus;
+    std::lock_guard<std::mutex> lock(mu);
+    cache[key] = n;
+    *out = n;
+    return hipSuccess;
 }
 
 static thread_local LaunchEvents g_launch_events = {nullptr, nullptr};

@@ -19,9 +19,11 @@ __global__ __launch_bounds__(kCombineBlock) void combine_kernel(const u32x4* __r
                                                                 const float* __restrict__ w,
                                                                 u32x4* __restrict__ out, int64_t T,
                                                                 int32_t k, int64_t nvec,
-                                                                int64_t n_rows, uint32_t* status) {
+                                                                int64_t n_rows, uint32_t* status,
+                                                                uint32_t n_static) {
     constexpr int TPB = kCombineBlock / G;
-    const int64_t t = (int64_t)blockIdx.x * TPB + threadIdx.x / G;
+    const uint32_t blk = claim_block(status + kHdrCombineTicket, n_static, status);
+    const int64_t t = (int64_t)blk * TPB + threadIdx.x / G;
     if (t >= T) return;
     combine_row<G, VPT, kSlotBatch>(y, pos, w, out, t, k, nvec, n_rows, threadIdx.x % G, status);
 }
@@ -33,9 +35,15 @@ hipError_t launch_combine(const Plan& p, const void* y, const int32_t* pos, cons
     auto go = [&]<int GG, int VV>() -> hipError_t {
         constexpr int TPB = kCombineBlock / GG;
         const int64_t blocks = (p.T + TPB - 1) / TPB;
+        int64_t n_static = 0;
+        const hipError_t e = resident_blocks(reinterpret_cast<const void*>(combine_kernel<GG, VV>),
+                                             kCombineBlock, 0, &n_static);
+        if (e != hipSuccess) return e;
+        if (n_static > blocks) n_static = blocks;
         return launch_kernel(combine_kernel<GG, VV>, dim3((unsigned)blocks), dim3(kCombineBlock), 0,
                              stream, static_cast<const u32x4*>(y), pos, topk_w,
-                             static_cast<u32x4*>(out), p.T, p.k, p.H / 8, p.rows, status);
+                             static_cast<u32x4*>(out), p.T, p.k, p.H / 8, p.rows, status,
+                             (uint32_t)n_static);
     };
     return with_group(G, VPT, go);
 }

@@ -131,6 +131,29 @@ __device__ __forceinline__ void raise_status(uint32_t* status, uint32_t code) {
 }
 
 // Constant-rate device clock used for bounded waits.
+// Block of work of this workgroup.  The first n_static workgroups (about the
+// ones that fit on the chip at once, which start together) take their own
+// index.  Later workgroups start one by one as slots free up and take the next
+// ticket of *ctr: blocks then go out in the order workgroups start, whichever
+// XCD runs them, so the rows in flight stay close together in memory even
+// when the XCDs drift apart.  The workgroup that draws the last ticket (all
+// others have drawn theirs) resets *ctr for the next call.  A ticket past the
+// end means a call that never finished left *ctr behind: the workgroup then
+// gets no block and reports UBEP_ERR_WORKSPACE.
+__device__ __forceinline__ uint32_t claim_block(uint32_t* ctr, uint32_t n_static, uint32_t* status) {
+    __shared__ uint32_t s_block;
+    if (blockIdx.x < n_static) return blockIdx.x;      // uniform across the workgroup
+    if (threadIdx.x == 0) {
+        const uint32_t n_dyn = gridDim.x - n_static;
+        const uint32_t tk = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (tk == n_dyn - 1u) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (tk >= n_dyn) raise_status(status, UBEP_ERR_WORKSPACE);
+        s_block = tk < n_dyn ? n_static + tk : gridDim.x;
+    }
+    __syncthreads();
+    return s_block;
+}
+
 __device__ __forceinline__ uint64_t now_ticks() { return wall_clock64(); }
 
 }  // namespace ubep

@@ -16,9 +16,11 @@ __global__ __launch_bounds__(kRowBlock) void dispatch_bf16_kernel(const u32x4* _
                                                                   const int32_t* __restrict__ pos,
                                                                   u32x4* __restrict__ recv,
                                                                   int64_t T, int32_t k, int64_t nvec,
-                                                                  int64_t n_rows, uint32_t* status) {
+                                                                  int64_t n_rows, uint32_t* status,
+                                                                  uint32_t n_static) {
     constexpr int TPB = kRowBlock / G;
-    const int64_t t = (int64_t)blockIdx.x * TPB + threadIdx.x / G;
+    const uint32_t blk = claim_block(status + kHdrDispatchTicket, n_static, status);
+    const int64_t t = (int64_t)blk * TPB + threadIdx.x / G;
     if (t >= T) return;
     dispatch_row_bf16<G, VPT, NT>(x, pos, recv, t, k, nvec, n_rows, threadIdx.x % G, status);
 }
@@ -29,9 +31,11 @@ __global__ __launch_bounds__(kRowBlock) void dispatch_fp8_kernel(const u32x4* __
                                                                  u32x4* __restrict__ recv8,
                                                                  float* __restrict__ recv_scale,
                                                                  int64_t T, int32_t k, int64_t H,
-                                                                 int64_t n_rows, uint32_t* status) {
+                                                                 int64_t n_rows, uint32_t* status,
+                                                                 uint32_t n_static) {
     constexpr int TPB = kRowBlock / G;
-    const int64_t t = (int64_t)blockIdx.x * TPB + threadIdx.x / G;
+    const uint32_t blk = claim_block(status + kHdrDispatchTicket, n_static, status);
+    const int64_t t = (int64_t)blk * TPB + threadIdx.x / G;
     if (t >= T) return;
     dispatch_row_fp8<G>(x, pos, recv8, recv_scale, t, k, H, n_rows, threadIdx.x % G, status);
 }
@@ -43,9 +47,15 @@ hipError_t launch_dispatch_bf16(const Plan& p, const void* x, const int32_t* pos
     auto go = [&]<int GG, int VV>() -> hipError_t {
         constexpr int TPB = kRowBlock / GG;
         const int64_t blocks = (p.T + TPB - 1) / TPB;
+        int64_t n_static = 0;
+        const hipError_t e = resident_blocks(
+            reinterpret_cast<const void*>(dispatch_bf16_kernel<GG, VV, false>), kRowBlock, 0, &n_static);
+        if (e != hipSuccess) return e;
+        if (n_static > blocks) n_static = blocks;
         return launch_kernel(dispatch_bf16_kernel<GG, VV, false>, dim3((unsigned)blocks),
                              dim3(kRowBlock), 0, stream, static_cast<const u32x4*>(x), pos,
-                             static_cast<u32x4*>(recv), p.T, p.k, p.H / 8, p.rows, status);
+                             static_cast<u32x4*>(recv), p.T, p.k, p.H / 8, p.rows, status,
+                             (uint32_t)n_static);
     };
     return with_group(G, VPT, go);
 }
@@ -55,9 +65,14 @@ static hipError_t launch_fp8_g(const Plan& p, const void* x, const int32_t* pos,
                                float* recv_scale, uint32_t* status, hipStream_t stream) {
     constexpr int TPB = kRowBlock / G;
     const int64_t blocks = (p.T + TPB - 1) / TPB;
+    int64_t n_static = 0;
+    const hipError_t e = resident_blocks(reinterpret_cast<const void*>(dispatch_fp8_kernel<G>),
+                                         kRowBlock, 0, &n_static);
+    if (e != hipSuccess) return e;
+    if (n_static > blocks) n_static = blocks;
     return launch_kernel(dispatch_fp8_kernel<G>, dim3((unsigned)blocks), dim3(kRowBlock), 0, stream,
                          static_cast<const u32x4*>(x), pos, static_cast<u32x4*>(recv8), recv_scale,
-                         p.T, p.k, p.H, p.rows, status);
+                         p.T, p.k, p.H, p.rows, status, (uint32_t)n_static);
 }
 
 hipError_t launch_dispatch_fp8(const Plan& p, const void* x, const int32_t* pos, void* recv8,

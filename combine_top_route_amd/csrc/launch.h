@@ -78,6 +78,10 @@ hipError_t launch_fill_zero(void* ws, size_t bytes, hipStream_t stream);
 
 hipError_t launch_clear_status(uint32_t* status, hipStream_t stream);
 
+// Workgroups of `kernel` (block threads, lds bytes of dynamic LDS) that fit on
+// the current device at once: blocks per CU times CUs (cached per kernel).
+hipError_t resident_blocks(const void* kernel, int block, size_t lds, int64_t* out);
+
 // Device properties used to size persistent grids and bounded waits.
 struct DeviceInfo {
     int cus;

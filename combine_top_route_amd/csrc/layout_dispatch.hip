@@ -5,15 +5,21 @@
 // starting the reorder as soon as the metadata is there, with no global
 // barrier between the stages).
 //
-// Every workgroup first takes a role ticket.  The first n_workers tickets
-// run the layout worker (layout_worker.h); they write pos with
-// device-coherent stores and then bump a "positions ready" counter.  Every
-// other ticket is a data worker for a block of tokens: it loads its tokens'
-// rows of x into registers while the layout runs, polls the counter, reads
-// its positions with device-coherent loads and stores the rows into the
-// receive regions.  Layout workers hold the first tickets, so they are
-// running before any data worker waits on them: no deadlock for any grid.
-// The result equals ubep_layout followed by ubep_dispatch(UBEP_BF16).
+// Every workgroup moves the rows of one block of tokens (its block index for
+// the workgroups that start together, the next block ticket for later ones).
+// The first n_workers workgroups to find layout roles left also run the layout
+// worker (layout_worker.h) first: a workgroup reads the role counter with a
+// plain load and takes a role with an atomic only while the count is below
+// n_workers, so the other workgroups never queue on that word.  Layout
+// workers write pos with device-coherent stores and bump a "positions ready"
+// counter; every workgroup loads its tokens' rows of x (data-only workgroups
+// while the layout runs), polls the counter, reads its positions with
+// device-coherent loads and stores the rows into the receive regions.
+// A workgroup is data-only only once all n_workers roles are taken, by
+// workgroups that were running when they took them and whose layout work
+// never waits on row movement: no deadlock for any grid of at least n_workers
+// workgroups.  The result equals ubep_layout followed by
+// ubep_dispatch(UBEP_BF16).
 #include "launch.h"
 #include "layout_worker.h"
 #include "rows.h"
@@ -29,7 +35,8 @@ template <int G, int VPT, int LR>
 __global__ __launch_bounds__(kFusedThreads) void layout_dispatch_kernel(LayoutArgs la,
                                                                        const u32x4* __restrict__ x,
                                                                        u32x4* __restrict__ recv,
-                                                                       uint32_t n_workers) {
+                                                                       uint32_t n_workers,
+                                                                       uint32_t n_static) {
     extern __shared__ int32_t dyn_lds[];
     __shared__ uint32_t s_role;
     __shared__ int32_t s_pos[kFusedThreads / 64 * kMaxK];
@@ -37,66 +44,76 @@ __global__ __launch_bounds__(kFusedThreads) void layout_dispatch_kernel(LayoutAr
     const int tid = threadIdx.x;
     uint32_t* status = &la.hdr[kHdrStatus];
     const uint32_t epoch = ld_relaxed(&la.hdr[kHdrLayoutEpoch]);
-    if (tid == 0) s_role = add_relaxed(&la.hdr[kHdrRoleTicket], 1u);
+    if (tid == 0) {
+        uint32_t role = 0xFFFFFFFFu;
+        if (ld_relaxed(&la.hdr[kHdrRoleTicket]) < n_workers) {
+            const uint32_t r = add_relaxed(&la.hdr[kHdrRoleTicket], 1u);
+            if (r < n_workers) role = r;
+        }
+        s_role = role;
+    }
     __syncthreads();
     const uint32_t role = s_role;
+    const bool worker = role < n_workers;
 
-    if (role < n_workers) {
+    if (worker) {
         const LayoutLds L = carve_lds(dyn_lds, p, kFusedWaves);
         layout_worker<kFusedWaves, LR, true, kFusedWindow>(la, L, epoch, role, n_workers);
         wait_memory();                 // this workgroup's positions are at the coherent level
         __syncthreads();
         if (tid == 0) add_relaxed(&la.hdr[kHdrPosReady], 1u);
-    } else {
-        constexpr int TPB = kFusedThreads / G;
-        const int grp = tid / G, gtid = tid % G;
-        const int64_t t = (int64_t)(role - n_workers) * TPB + grp;
-        const bool live = t < p.T;
-        const int64_t nvec = p.H / 8;
-        const u32x4* xr = x + (live ? t : 0) * nvec;
-        // the first pass of the row, loaded while the layout runs
-        u32x4 buf[VPT];
+    }
+
+    constexpr int TPB = kFusedThreads / G;
+    const int grp = tid / G, gtid = tid % G;
+    const uint32_t blk = claim_block(&la.hdr[kHdrFusedBlockTicket], n_static, status);
+    const int64_t t = (int64_t)blk * TPB + grp;
+    const bool live = t < p.T;
+    const int64_t nvec = p.H / 8;
+    const u32x4* xr = x + (live ? t : 0) * nvec;
+    // the first pass of the row (loaded while the layout runs, for data-only
+    // workgroups)
+    u32x4 buf[VPT];
 #pragma unroll
-        for (int i = 0; i < VPT; ++i) {
-            const int64_t v = gtid + (int64_t)i * G;
-            if (live && v < nvec) buf[i] = xr[v];
-        }
-        if (tid == 0) {
-            const uint64_t t0 = now_ticks();
-            while (ld_relaxed(&la.hdr[kHdrPosReady]) < n_workers) {
-                if (now_ticks() - t0 > la.spin_ticks) {
-                    raise_status(status, UBEP_ERR_TIMEOUT);
-                    break;
-                }
-                __builtin_amdgcn_s_sleep(2);
+    for (int i = 0; i < VPT; ++i) {
+        const int64_t v = gtid + (int64_t)i * G;
+        if (live && v < nvec) buf[i] = xr[v];
+    }
+    if (tid == 0) {
+        const uint64_t t0 = now_ticks();
+        while (ld_relaxed(&la.hdr[kHdrPosReady]) < n_workers) {
+            if (now_ticks() - t0 > la.spin_ticks) {
+                raise_status(status, UBEP_ERR_TIMEOUT);
+                break;
             }
+            __builtin_amdgcn_s_sleep(2);
         }
-        __syncthreads();
-        if (live && gtid < p.k)
-            s_pos[grp * kMaxK + gtid] = __hip_atomic_load(la.pos + t * p.k + gtid, __ATOMIC_RELAXED,
-                                                          __HIP_MEMORY_SCOPE_AGENT);
-        __syncthreads();
-        if (live) {
-            for (int64_t v0 = 0; v0 < nvec; v0 += (int64_t)G * VPT) {
-                if (v0 > 0) {
+    }
+    __syncthreads();
+    if (live && gtid < p.k)
+        s_pos[grp * kMaxK + gtid] = __hip_atomic_load(la.pos + t * p.k + gtid, __ATOMIC_RELAXED,
+                                                      __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    if (live) {
+        for (int64_t v0 = 0; v0 < nvec; v0 += (int64_t)G * VPT) {
+            if (v0 > 0) {
 #pragma unroll
-                    for (int i = 0; i < VPT; ++i) {
-                        const int64_t v = v0 + gtid + (int64_t)i * G;
-                        if (v < nvec) buf[i] = xr[v];
-                    }
+                for (int i = 0; i < VPT; ++i) {
+                    const int64_t v = v0 + gtid + (int64_t)i * G;
+                    if (v < nvec) buf[i] = xr[v];
                 }
-                for (int32_t j = 0; j < p.k; ++j) {
-                    const int32_t q = s_pos[grp * kMaxK + j];
-                    if (!row_ok(q, p.rows)) {
-                        if (gtid == 0 && v0 == 0) raise_status(status, UBEP_ERR_BAD_POSITION);
-                        continue;
-                    }
-                    u32x4* dst = recv + (int64_t)q * nvec;
+            }
+            for (int32_t j = 0; j < p.k; ++j) {
+                const int32_t q = s_pos[grp * kMaxK + j];
+                if (!row_ok(q, p.rows)) {
+                    if (gtid == 0 && v0 == 0) raise_status(status, UBEP_ERR_BAD_POSITION);
+                    continue;
+                }
+                u32x4* dst = recv + (int64_t)q * nvec;
 #pragma unroll
-                    for (int i = 0; i < VPT; ++i) {
-                        const int64_t v = v0 + gtid + (int64_t)i * G;
-                        if (v < nvec) dst[v] = buf[i];
-                    }
+                for (int i = 0; i < VPT; ++i) {
+                    const int64_t v = v0 + gtid + (int64_t)i * G;
+                    if (v < nvec) dst[v] = buf[i];
                 }
             }
         }
@@ -149,10 +166,17 @@ hipError_t launch_layout_dispatch(const Plan& p, const int32_t* idx, const void*
     const int64_t lane_need = (p.tile_rows + kFusedWaves * 64 - 1) / (kFusedWaves * 64);
     auto go = [&]<int GG, int VV>() -> hipError_t {
         constexpr int TPB = kFusedThreads / GG;
-        const int64_t grid = n_workers + (p.T + TPB - 1) / TPB;
-        const auto one = [&](auto kernel) {
+        int64_t grid = (p.T + TPB - 1) / TPB;     // one block of tokens per workgroup
+        if (grid < (int64_t)n_workers) grid = n_workers;
+        const auto one = [&](auto kernel) -> hipError_t {
+            int64_t n_static = 0;
+            const hipError_t err = resident_blocks(reinterpret_cast<const void*>(kernel), kFusedThreads,
+                                                   lds, &n_static);
+            if (err != hipSuccess) return err;
+            if (n_static > grid) n_static = grid;
             return launch_kernel(kernel, dim3((unsigned)grid), dim3(kFusedThreads), lds, stream, a,
-                                 static_cast<const u32x4*>(x), static_cast<u32x4*>(recv), n_workers);
+                                 static_cast<const u32x4*>(x), static_cast<u32x4*>(recv), n_workers,
+                                 (uint32_t)n_static);
         };
         if (lane_need <= 4) return one(layout_dispatch_kernel<GG, VV, 4>);
         if (lane_need <= 8) return one(layout_dispatch_kernel<GG, VV, 8>);

@@ -31,7 +31,10 @@ constexpr int kHdrLayoutDone = 128;    // workgroups finished in the layout
 constexpr int kHdrLayoutEpoch = 160;   // layout calls completed (tags look-back state)
 constexpr int kHdrRoleTicket = 192;    // role ticket of the fused layout + dispatch kernel
 constexpr int kHdrPosReady = 224;      // layout workers whose positions are stored
-constexpr size_t kHdrBytes = 1024;
+constexpr int kHdrCombineTicket = 256; // block ticket of the combine's later workgroups
+constexpr int kHdrDispatchTicket = 288; // block ticket of the dispatch's later workgroups
+constexpr int kHdrFusedBlockTicket = 320; // block ticket of the fused launch's later workgroups
+constexpr size_t kHdrBytes = 2048;
 constexpr int kFlagStride = 32;        // uint32 per chunk ready flag (128 bytes)
 
 // Look-back state word (64 bits): the layout call's epoch in the high half;

@@ -72,7 +72,9 @@ typedef enum ubep_status {
     UBEP_ERR_BAD_EXPERT_ID = 3,   /* device: a topk_idx entry outside [0, E)        */
     UBEP_ERR_TIMEOUT = 4,         /* device: a bounded wait on a ready flag expired */
     UBEP_ERR_HIP = 5,             /* a HIP runtime call failed                      */
-    UBEP_ERR_BAD_POSITION = 6     /* device: a pos entry outside [0, T*k)           */
+    UBEP_ERR_BAD_POSITION = 6,    /* device: a pos entry outside [0, T*k)           */
+    UBEP_ERR_WORKSPACE = 7        /* device: workspace counters left inconsistent by
+                                     a call that never finished; re-initialize it  */
 } ubep_status;
 
 typedef enum ubep_dtype {
@@ -94,7 +96,9 @@ ubep_status ubep_check_shape(const ubep_shape *shape /*host*/, int dtype);
  * invalid).  The workspace holds the device status word, the layout's tile
  * counters and look-back state, and the chunk pipeline's task counter and
  * per-chunk ready flags.  It must be zero-filled before its first use (for
- * example with ubep_workspace_init); every call leaves it ready for the next. */
+ * example with ubep_workspace_init); every call leaves it ready for the next.
+ * A workspace serves one call at a time: calls that share one must be ordered
+ * (the same stream, or synchronised streams). */
 size_t ubep_workspace_bytes(const ubep_shape *shape /*host*/);
 
 /* Zero-fill `ws_bytes` bytes of workspace with a fill kernel on `stream`.

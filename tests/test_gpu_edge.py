@@ -209,3 +209,49 @@ def test_launch_timing_events_time_the_kernel_and_change_nothing():
     assert 0.0 < us < 10000.0, us
     np.testing.assert_array_equal(to_np(b.out), ref)
     assert device_status(b) == ubep.OK
+
+
+def _exact_path(w, b):
+    s = w.shape
+    L = oracle.layout(w.topk_idx, s.E, s.R, s.C)
+    y = oracle.dispatch_bf16(w.x, L["pos"])
+    out = oracle.combine(y, L["pos"], w.topk_w)
+    b.out.zero_()
+    run_path(b)
+    torch.cuda.synchronize()
+    assert device_status(b) == ubep.OK
+    np.testing.assert_array_equal(to_np(b.recv), y)
+    np.testing.assert_array_equal(to_np(b.out), out)
+
+
+def test_block_tickets_reset_across_grids():
+    """Dispatch and combine hand their later workgroups token blocks from
+    ticket counters in the workspace; grids larger than the chip holds use
+    them, and alternating grid sizes on one workspace must stay exact."""
+    shapes = [dict(T=16384, H=64, E=64, k=4, R=16), dict(T=12288, H=128, E=32, k=4, R=8),
+              dict(T=16384, H=64, E=64, k=4, R=16)]
+    nws = max(ubep.ubep_workspace_bytes(dict(C=1, **s)) for s in shapes)
+    ws = torch.zeros(nws, dtype=torch.uint8, device="cuda")
+    for i, sh in enumerate(shapes):
+        w = custom(seed=50 + i, **sh)
+        b = upload(w)
+        b.ws = ws
+        say(f"block tickets {sh}")
+        _exact_path(w, b)
+
+
+def test_stale_block_ticket_is_reported_and_init_recovers():
+    w = custom(T=16384, H=64, E=64, k=4, R=16, seed=60)
+    b = upload(w)
+    s = w.shape.as_dict()
+    ubep.ubep_layout(s, b.topk_idx, b.pos, b.expert_count, b.rank_count, b.recv_offset,
+                     b.send_offset, None, None, b.ws)
+    ubep.ubep_dispatch(s, ubep.BF16, b.x, b.pos, b.recv, None, b.ws)
+    torch.cuda.synchronize()
+    assert device_status(b) == ubep.OK
+    b.ws.view(torch.int32)[256] = 1 << 30          # the combine's ticket word, left behind
+    say("stale combine ticket")
+    ubep.ubep_combine(s, b.y, b.pos, b.topk_w, b.out, b.ws)
+    assert device_status(b) == ubep.ERR_WORKSPACE
+    ubep.ubep_workspace_init(b.ws)
+    _exact_path(w, b)
