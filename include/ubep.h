@@ -133,7 +133,8 @@ ubep_status ubep_layout(const ubep_shape *shape /*host*/, const int32_t *topk_id
 /* Layout and bf16 dispatch in one launch ("Kernel Decomposition": a few
  * workgroups compute the layout and publish it to global memory while the
  * others load their token rows and poll for it, instead of a barrier between
- * the two stages).  Outputs and errors are exactly those of ubep_layout
+ * the two stages).  Every workgroup moves one block of tokens; the first few
+ * to start also run the layout before their rows.  Outputs and errors are exactly those of ubep_layout
  * followed by ubep_dispatch(UBEP_BF16) on the same stream; the caller's pos is
  * both an output and the dispatch's input.  Shapes whose layout needs more
  * than 24 KB of LDS per workgroup run as those two launches. */
