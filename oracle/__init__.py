@@ -34,6 +34,8 @@ def lib():
         L.oracle_check_shape.restype = C.c_int
         L.oracle_layout.argtypes = [i64, i32, i32, i32, i32, p, p, p, p, p, p, p, p]
         L.oracle_layout.restype = C.c_int
+        L.oracle_layout_grouped.argtypes = [i64, i32, i32, i32, i32, p, p, p, p, p, p, p, p, p]
+        L.oracle_layout_grouped.restype = C.c_int
         L.oracle_dispatch_bf16.argtypes = [i64, i64, i32, p, p, p]
         L.oracle_dispatch_bf16.restype = None
         L.oracle_dispatch_fp8.argtypes = [i64, i64, i32, p, p, p, p]
@@ -85,6 +87,31 @@ def layout(topk_idx: np.ndarray, E: int, R: int, C: int = 1, want_src: bool = Tr
                              _p(out["rank_count"]), _p(out["recv_offset"]),
                              _p(out["send_offset"]), _p(out["chunk_offset"]),
                              _p(out["recv_src"]))
+    if st != OK:
+        raise OracleError(st)
+    return out
+
+
+def layout_grouped(topk_idx: np.ndarray, E: int, R: int, C: int = 1, want_src: bool = True) -> dict:
+    """Expert-grouped layout: rows of each region in (expert, token, slot)
+    order, plus expert_offset [E+1]."""
+    idx = np.ascontiguousarray(topk_idx, dtype=np.int32)
+    T, k = idx.shape
+    out = dict(
+        pos=np.empty((T, k), np.int32),
+        expert_count=np.empty(E, np.int32),
+        expert_offset=np.empty(E + 1, np.int32),
+        rank_count=np.empty(R, np.int32),
+        recv_offset=np.empty(R + 1, np.int32),
+        send_offset=np.empty((R, R), np.int32),
+        chunk_offset=np.empty((C, R), np.int32),
+        recv_src=np.empty(T * k, np.int32) if want_src else None,
+    )
+    st = lib().oracle_layout_grouped(T, E, k, R, C, _p(idx), _p(out["pos"]),
+                                     _p(out["expert_count"]), _p(out["expert_offset"]),
+                                     _p(out["rank_count"]), _p(out["recv_offset"]),
+                                     _p(out["send_offset"]), _p(out["chunk_offset"]),
+                                     _p(out["recv_src"]))
     if st != OK:
         raise OracleError(st)
     return out

@@ -146,6 +146,90 @@ int oracle_layout(int64_t T, int32_t E, int32_t k, int32_t R, int32_t C,
     return ORACLE_OK;
 }
 
+/* Expert-grouped layout: the same counts and offsets as oracle_layout, but
+ * the rows inside each rank's region are ordered by (expert, token, slot),
+ * so each expert's rows are one contiguous run -- the order a grouped expert
+ * computation reads.  (The pages fix only that each token goes to the
+ * device of each expert it selected and comes back; the order inside a
+ * region is this build's choice.)  Experts of rank d are E/R consecutive
+ * ids, so the runs of rank d's experts tile region d in expert order:
+ *   expert_offset[e] = sum of expert_count[e'] for e' < e  (E+1 entries),
+ *   pos[t][j]        = expert_offset[e] + #{(t', j') < (t, j) : idx = e},
+ *   recv_offset[d]   = expert_offset[d * E/R].
+ * send_offset and chunk_offset keep their meaning as row counts
+ * (rows to rank d from earlier source ranks / chunks). */
+int oracle_layout_grouped(int64_t T, int32_t E, int32_t k, int32_t R, int32_t C,
+                          const int32_t *topk_idx,
+                          int32_t *pos, int32_t *expert_count, int32_t *expert_offset,
+                          int32_t *rank_count, int32_t *recv_offset, int32_t *send_offset,
+                          int32_t *chunk_offset, int32_t *recv_src)
+{
+    int st = oracle_check_shape(T, 8, E, k, R, C, 0);
+    if (st != ORACLE_OK) return st;
+    for (int64_t i = 0; i < T * k; ++i)
+        if (topk_idx[i] < 0 || topk_idx[i] >= E) return ORACLE_BAD_EXPERT_ID;
+
+    const int32_t epr = E / R;
+    const int64_t tps = T / R;
+    const int64_t tpc = T / C;
+
+    int32_t *sd_count = calloc((size_t)R * R, sizeof(int32_t));
+    int32_t *cd_count = calloc((size_t)C * R, sizeof(int32_t));
+    int32_t *cursor = calloc((size_t)E, sizeof(int32_t));
+    if (!sd_count || !cd_count || !cursor) {
+        free(sd_count); free(cd_count); free(cursor);
+        return ORACLE_UNSUPPORTED;
+    }
+
+    /* 1. token counts per expert, per rank, per (source, rank), per (chunk, rank) */
+    for (int32_t e = 0; e < E; ++e) expert_count[e] = 0;
+    for (int32_t d = 0; d < R; ++d) rank_count[d] = 0;
+    for (int64_t t = 0; t < T; ++t) {
+        for (int32_t j = 0; j < k; ++j) {
+            int32_t e = topk_idx[t * k + j];
+            int32_t d = e / epr;
+            expert_count[e] += 1;
+            rank_count[d] += 1;
+            sd_count[(t / tps) * R + d] += 1;
+            cd_count[(t / tpc) * R + d] += 1;
+        }
+    }
+
+    /* 2. exclusive prefix sums: over experts, then the rank starts from them */
+    expert_offset[0] = 0;
+    for (int32_t e = 0; e < E; ++e) expert_offset[e + 1] = expert_offset[e] + expert_count[e];
+    for (int32_t d = 0; d <= R; ++d) recv_offset[d] = expert_offset[d * epr];
+    for (int32_t d = 0; d < R; ++d) {
+        int32_t run = 0;
+        for (int32_t s = 0; s < R; ++s) {
+            send_offset[s * R + d] = run;
+            run += sd_count[s * R + d];
+        }
+    }
+    if (chunk_offset) {
+        for (int32_t d = 0; d < R; ++d) {
+            int32_t run = 0;
+            for (int32_t c = 0; c < C; ++c) {
+                chunk_offset[c * R + d] = run;
+                run += cd_count[c * R + d];
+            }
+        }
+    }
+
+    /* 3. stable positions: rows in (expert, token, slot) order */
+    for (int32_t e = 0; e < E; ++e) cursor[e] = expert_offset[e];
+    for (int64_t t = 0; t < T; ++t) {
+        for (int32_t j = 0; j < k; ++j) {
+            int32_t p = cursor[topk_idx[t * k + j]]++;
+            pos[t * k + j] = p;
+            if (recv_src) recv_src[p] = (int32_t)(t * k + j);
+        }
+    }
+
+    free(sd_count); free(cd_count); free(cursor);
+    return ORACLE_OK;
+}
+
 /* ------------------------------------------------------------------------ */
 /* number formats                                                           */
 /* ------------------------------------------------------------------------ */

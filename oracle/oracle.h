@@ -10,6 +10,10 @@ int oracle_check_shape(int64_t T, int64_t H, int32_t E, int32_t k, int32_t R, in
 int oracle_layout(int64_t T, int32_t E, int32_t k, int32_t R, int32_t C, const int32_t *topk_idx,
                   int32_t *pos, int32_t *expert_count, int32_t *rank_count, int32_t *recv_offset,
                   int32_t *send_offset, int32_t *chunk_offset, int32_t *recv_src);
+int oracle_layout_grouped(int64_t T, int32_t E, int32_t k, int32_t R, int32_t C,
+                          const int32_t *topk_idx, int32_t *pos, int32_t *expert_count,
+                          int32_t *expert_offset, int32_t *rank_count, int32_t *recv_offset,
+                          int32_t *send_offset, int32_t *chunk_offset, int32_t *recv_src);
 float oracle_bf16_to_f32(uint16_t b);
 uint16_t oracle_f32_to_bf16(float f);
 float oracle_e4m3_to_f32(uint8_t c);
