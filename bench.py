@@ -5,7 +5,8 @@ One step = the whole path over one synthetic batch already resident in HBM:
 ubep_layout (counts, prefix sums, positions) -> ubep_dispatch (rows into the
 R receive regions) -> identity expert (y = recv) -> ubep_combine (slot-ordered
 FMA chain back to token order).  `--mode chunked` runs layout + the one-kernel
-chunk pipeline instead of the two row kernels.
+chunk pipeline instead of the two row kernels; `--order expert` takes the layout
+from ubep_layout_grouped (rows of each region grouped by expert).
 
 Throughput counts algorithmic bytes (what the path must read and write):
   layout   4Tk (ids) + 4Tk (positions)
@@ -196,6 +197,9 @@ def main(argv=None):
     ap.add_argument("--mode", choices=["unfused", "chunked", "gated", "fused"], default="unfused",
                     help="gated: the step starts from router logits (ubep_gate, then unfused); "
                          "fused: ubep_layout_dispatch (one launch), then combine")
+    ap.add_argument("--order", choices=["rank", "expert"], default="rank",
+                    help="receive order inside a rank's region: (token, slot) with ubep_layout, or "
+                         "expert-grouped (expert, token, slot) with ubep_layout_grouped")
     ap.add_argument("--cold", action="store_true",
                     help="headline the cold-cache pass (the warm one is then reported beside it)")
     ap.add_argument("--cpu-reps", type=int, default=7)
@@ -232,10 +236,14 @@ def main(argv=None):
     if args.mode == "chunked" and fp8:
         print("the chunk pipeline carries a bf16 payload only", file=sys.stderr)
         return 2
+    if args.mode == "fused" and args.order == "expert":
+        print("the fused launch computes the rank-order layout only", file=sys.stderr)
+        return 2
     torch.cuda.set_device(0)
     b = alloc_buffers(sd, dtype, "cuda", x_bits=w.x, topk_idx=w.topk_idx, topk_w=w.topk_w)
     stream = torch.cuda.current_stream()
     chunk_off = b.chunk_offset if s.C > 1 else None
+    expert_off = torch.empty(s.E + 1, dtype=torch.int32, device="cuda")
     # cold-cache pass: reading 512 MB of unrelated data between steps evicts the
     # path's arrays from the 256 MB memory-side cache and the L2s and leaves
     # clean lines behind (a write scrub would leave dirty lines that the next
@@ -262,6 +270,9 @@ def main(argv=None):
         stream = torch.cuda.current_stream()    # the capture stream while a graph records
         if name == "gate":
             ubep.ubep_gate(s.T, s.E, s.k, logits, b.topk_idx, b.topk_w, stream=stream, **gate_args)
+        elif name == "layout" and args.order == "expert":
+            ubep.ubep_layout_grouped(sd, b.topk_idx, b.pos, b.expert_count, expert_off, b.rank_count,
+                                     b.recv_offset, b.send_offset, chunk_off, None, b.ws, stream)
         elif name == "layout":
             ubep.ubep_layout(sd, b.topk_idx, b.pos, b.expert_count, b.rank_count, b.recv_offset,
                              b.send_offset, chunk_off, None, b.ws, stream)
@@ -444,6 +455,7 @@ def main(argv=None):
         "dtype": "fp8_e4m3+bf16" if fp8 else "bf16",
         "data": "synthetic",
         "config": {"workload": name, **sd, "payload": w.recipe.payload, "mode": args.mode,
+                   "order": args.order,
                    "caches": ("cold: 512 MB read between steps" if args.cold
                               else "warm: back-to-back steps"),
                    "seed": w.recipe.seed},

@@ -9,7 +9,8 @@ from ._abi import (BF16, ERR_BAD_EXPERT_ID, ERR_BAD_POSITION, ERR_HIP, ERR_INVAL
                    UbepError, lib, status_str, ubep_abi_version, ubep_check_shape, ubep_combine,
                    ubep_copy, ubep_dispatch, ubep_gate, ubep_gate_shape,
                    ubep_dispatch_combine_chunked, ubep_get_device_status, ubep_identity_expert_fp8,
-                   ubep_layout, ubep_layout_dispatch, ubep_set_layout_workers, ubep_shape,
+                   ubep_layout, ubep_layout_dispatch, ubep_layout_grouped, ubep_set_layout_workers,
+                   ubep_shape,
                    ubep_time_next_launch, ubep_workspace_bytes, ubep_workspace_init)
 from .buffers import Buffers, alloc_buffers
 

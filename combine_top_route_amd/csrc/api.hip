@@ -27,7 +27,7 @@ static size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 // A layout tile holds whole tokens and never straddles a source-rank or chunk
 // boundary: its token count divides gcd(T/R, T/C).  Take the largest such
 // divisor with at most kTileRowsMax rows.
-void make_plan(const ubep_shape& s, Plan* p) {
+void make_plan(const ubep_shape& s, Plan* p, int order) {
     p->T = s.T;
     p->H = s.H;
     p->E = s.E;
@@ -57,14 +57,21 @@ void make_plan(const ubep_shape& s, Plan* p) {
     p->dbits = bits_for(s.R);
     p->ebits = bits_for(s.E);
     p->slots = s.R + s.E;
-    p->gather = (p->n_tiles * s.R <= kGatherMaxWords && p->n_tiles <= kGatherMaxTiles) ? 1 : 0;
+    p->order = order;
+    p->K = order ? s.E : s.R;
+    p->key_magic = order ? 0u : p->epr_magic;
+    p->kbits = order ? p->ebits : p->dbits;
+    p->kcol = order ? s.R : 0;
+    p->gather = (p->n_tiles * p->K <= kGatherMaxWords && p->n_tiles <= kGatherMaxTiles) ? 1 : 0;
+    // per-tile key arrays are sized for the larger key count (E >= R), so one
+    // workspace serves both orders
     size_t off = align_up(kHdrBytes, 256);
     p->off_state = off;
     off = align_up(off + (size_t)p->n_tiles * p->slots * 8, 256);
     p->off_excl = off;
-    off = align_up(off + (size_t)p->n_tiles * s.R * 4, 256);
+    off = align_up(off + (size_t)p->n_tiles * s.E * 4, 256);
     p->off_wbase = off;
-    off = align_up(off + (size_t)p->n_tiles * kLayoutWaves * s.R * 4, 256);
+    off = align_up(off + (size_t)p->n_tiles * kLayoutWaves * s.E * 4, 256);
     p->off_flags = off;
     off = align_up(off + (size_t)s.C * kFlagStride * 4, 256);
     p->ws_bytes = off;
@@ -83,10 +90,10 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 ubep_status hip_status(hipError_t e) { return e == hipSuccess ? UBEP_OK : UBEP_ERR_HIP; }
 
 // Shape check plus the tile-count limit of the layout's workspace.
-ubep_status check_and_plan(const ubep_shape* s, int dtype, Plan* p) {
+ubep_status check_and_plan(const ubep_shape* s, int dtype, Plan* p, int order = 0) {
     const ubep_status st = ubep_check_shape(s, dtype);
     if (st != UBEP_OK) return st;
-    make_plan(*s, p);
+    make_plan(*s, p, order);
     if (p->n_tiles > kMaxTiles || p->n_tiles * p->slots > kMaxStateWords) return UBEP_ERR_UNSUPPORTED;
     return UBEP_OK;
 }
@@ -163,8 +170,29 @@ ubep_status ubep_layout(const ubep_shape* s, const int32_t* topk_idx, int32_t* p
     uint64_t ticks;
     const ubep_status ts = spin_ticks_for(0, &ticks);
     if (ts != UBEP_OK) return ts;
-    return hip_status(launch_layout(p, topk_idx, pos, expert_count, rank_count, recv_offset,
-                                    send_offset, chunk_offset, recv_src, ws, ticks, stream));
+    return hip_status(launch_layout(p, topk_idx, pos, expert_count, nullptr, rank_count,
+                                    recv_offset, send_offset, chunk_offset, recv_src, ws, ticks,
+                                    stream));
+}
+
+ubep_status ubep_layout_grouped(const ubep_shape* s, const int32_t* topk_idx, int32_t* pos,
+                                int32_t* expert_count, int32_t* expert_offset, int32_t* rank_count,
+                                int32_t* recv_offset, int32_t* send_offset, int32_t* chunk_offset,
+                                int32_t* recv_src, void* ws, size_t ws_bytes, hipStream_t stream) {
+    Plan p;
+    const ubep_status st = check_and_plan(s, UBEP_BF16, &p, 1);
+    if (st != UBEP_OK) return st;
+    if (!layout_lds_fits(p)) return UBEP_ERR_UNSUPPORTED;
+    if (!topk_idx || !pos || !expert_count || !expert_offset || !rank_count || !recv_offset ||
+        !send_offset || !ws)
+        return UBEP_ERR_INVALID_ARG;
+    if (ws_bytes < p.ws_bytes || !aligned(ws, 256)) return UBEP_ERR_INVALID_ARG;
+    uint64_t ticks;
+    const ubep_status ts = spin_ticks_for(0, &ticks);
+    if (ts != UBEP_OK) return ts;
+    return hip_status(launch_layout(p, topk_idx, pos, expert_count, expert_offset, rank_count,
+                                    recv_offset, send_offset, chunk_offset, recv_src, ws, ticks,
+                                    stream));
 }
 
 ubep_status ubep_layout_dispatch(const ubep_shape* s, const int32_t* topk_idx, const void* x,

@@ -39,12 +39,14 @@ hipError_t launch_kernel(void (*kernel)(P...), dim3 grid, dim3 block, size_t lds
                               ev.start, ev.stop, 0);
 }
 
+// expert_offset: [E+1] output of the expert order (p.order == 1), may be null.
 hipError_t launch_layout(const Plan& p, const int32_t* idx, int32_t* pos, int32_t* expert_count,
-                         int32_t* rank_count, int32_t* recv_offset, int32_t* send_offset,
-                         int32_t* chunk_offset, int32_t* recv_src, void* ws, uint64_t spin_ticks,
-                         hipStream_t stream);
+                         int32_t* expert_offset, int32_t* rank_count, int32_t* recv_offset,
+                         int32_t* send_offset, int32_t* chunk_offset, int32_t* recv_src, void* ws,
+                         uint64_t spin_ticks, hipStream_t stream);
 
 int64_t layout_workers(const Plan& p, int cus);
+bool layout_lds_fits(const Plan& p);
 void set_layout_worker_cap(int32_t n);   // 0: default
 
 hipError_t launch_layout_dispatch(const Plan& p, const int32_t* idx, const void* x, int32_t* pos,

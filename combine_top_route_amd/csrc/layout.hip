@@ -22,13 +22,15 @@ namespace ubep {
 // Every workgroup is a worker and counts itself done as soon as it has its
 // totals (the round trip overlaps the rest of phase B); the last one resets.
 // LR: ids a lane holds (tiles of at most kLayoutThreads * LR rows).
-template <int LR>
+// EORD: expert order (a.p.order == 1).
+template <int LR, bool EORD>
 __global__ __launch_bounds__(kLayoutThreads) void layout_kernel(LayoutArgs a) {
     extern __shared__ int32_t dyn_lds[];
     const uint32_t epoch = ld_relaxed(&a.hdr[kHdrLayoutEpoch]);
     const LayoutLds L = carve_lds(dyn_lds, a.p, kLayoutWaves);
     uint32_t done = 0;
-    layout_worker<kLayoutWaves, LR, false>(a, L, epoch, blockIdx.x, gridDim.x, &done);
+    layout_worker<kLayoutWaves, LR, false, kLookbackWindow, EORD>(a, L, epoch, blockIdx.x, gridDim.x,
+                                                                 &done);
     if (threadIdx.x == 0 && done == gridDim.x - 1u) layout_reset(a, epoch);
 }
 
@@ -37,10 +39,10 @@ constexpr int kSingleThreads = 1024;
 constexpr int kSingleWaves = kSingleThreads / 64;
 constexpr int kSingleSteps = 64;                 // 64-row steps a wave may own
 constexpr int64_t kSingleMaxRows = (int64_t)kSingleWaves * kSingleSteps * 64;
-constexpr int kSingleMaxR = 256;
+constexpr int kSingleMaxK = 256;
 constexpr int kSingleMaxE = 4096;
 constexpr int kSingleMaxTiles = 256;
-constexpr int kSingleMaxTileCounts = 8192;       // n_tiles * R
+constexpr int kSingleMaxTileCounts = 8192;       // n_tiles * K
 
 // Only tiny problems: above a few thousand rows one CU's ballot and LDS work
 // costs more than the persistent kernel's memory round trips.
@@ -49,23 +51,31 @@ constexpr int64_t kSingleUseRows = 4096;
 bool layout_fits_one_group(const Plan& p) {
     const int64_t tiles_per_wave = (p.n_tiles + kSingleWaves - 1) / kSingleWaves;
     return p.rows <= kSingleUseRows && p.rows <= kSingleMaxRows && p.tile_rows % 64 == 0 && p.n_tiles <= kSingleMaxTiles &&
-           p.n_tiles * p.R <= kSingleMaxTileCounts && p.R <= kSingleMaxR && p.E <= kSingleMaxE &&
+           p.n_tiles * p.K <= kSingleMaxTileCounts && p.K <= kSingleMaxK && p.E <= kSingleMaxE &&
            tiles_per_wave * p.tile_rows <= (int64_t)kSingleSteps * 64;
 }
 
 template <int STEPS>
 __global__ __launch_bounds__(kSingleThreads) void layout_single_kernel(LayoutArgs a) {
-    __shared__ int32_t s_tc[kSingleMaxTileCounts];  // [tile][rank]: counts, then row bases
+    __shared__ int32_t s_tc[kSingleMaxTileCounts];  // [tile][key]: counts, then row bases
     __shared__ int32_t s_eh[kSingleMaxE];           // expert counts
-    __shared__ int32_t s_tot[kSingleMaxR];          // rank totals
-    __shared__ int32_t s_off[kSingleMaxR];          // recv_offset
+    __shared__ int32_t s_tot[kSingleMaxK];          // key totals
+    __shared__ int32_t s_off[kSingleMaxK];          // exclusive scan of the key totals
     __shared__ int32_t s_tmp[kSingleWaves];
 
     const Plan& p = a.p;
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int32_t R = p.R, E = p.E;
-    for (int i = tid; i < p.n_tiles * R; i += kSingleThreads) s_tc[i] = 0;
+    const int32_t R = p.R, E = p.E, K = p.K, epr = p.epr;
+    const bool eord = p.order != 0;
+    // rows with a key of rank d in a per-key array v (rank order: v[d])
+    const auto rank_sum = [&](const int32_t* v, int32_t d) -> int32_t {
+        if (!eord) return v[d];
+        int32_t c = 0;
+        for (int32_t e = d * epr; e < (d + 1) * epr; ++e) c += v[e];
+        return c;
+    };
+    for (int i = tid; i < p.n_tiles * K; i += kSingleThreads) s_tc[i] = 0;
     for (int i = tid; i < E; i += kSingleThreads) s_eh[i] = 0;
 
     // wave w owns tiles [t_lo, t_hi): rows [r_lo, r_lo + 64 steps)
@@ -94,14 +104,14 @@ __global__ __launch_bounds__(kSingleThreads) void layout_single_kernel(LayoutArg
     }
     __syncthreads();
 
-    // pass 1: per-tile rank counts and expert counts (order-free: LDS atomics)
+    // pass 1: per-tile key counts and expert counts (order-free: LDS atomics)
     {
         int32_t tile = t_lo, in_tile = 0;
 #pragma unroll
         for (int i = 0; i < STEPS; ++i) {
             if (i >= steps) break;                           // uniform across the wave
             const uint32_t e = (uint32_t)ev[i];
-            atomicAdd(&s_tc[tile * R + rank_of(e, p.epr_magic)], 1);
+            atomicAdd(&s_tc[tile * K + rank_of(e, p.key_magic)], 1);
             atomicAdd(&s_eh[e], 1);
             if (++in_tile == steps_per_tile) {
                 in_tile = 0;
@@ -111,19 +121,19 @@ __global__ __launch_bounds__(kSingleThreads) void layout_single_kernel(LayoutArg
     }
     __syncthreads();
 
-    // exclusive prefix over tiles for every rank; the totals
-    for (int32_t d = tid; d < R; d += kSingleThreads) {
+    // exclusive prefix over tiles for every key; the totals
+    for (int32_t d = tid; d < K; d += kSingleThreads) {
         int32_t run = 0;
         for (int32_t t = 0; t < n_tiles; ++t) {
-            const int32_t c = s_tc[t * R + d];
-            s_tc[t * R + d] = run;
+            const int32_t c = s_tc[t * K + d];
+            s_tc[t * K + d] = run;
             run += c;
         }
         s_tot[d] = run;
     }
     __syncthreads();
-    {   // exclusive scan of the totals over ranks (R <= 1024: one rank per thread)
-        const int32_t mine = tid < R ? s_tot[tid] : 0;
+    {   // exclusive scan of the totals over keys (K <= 1024: one key per thread)
+        const int32_t mine = tid < K ? s_tot[tid] : 0;
         int32_t inc = mine;
 #pragma unroll
         for (int o = 1; o < 64; o <<= 1) {
@@ -134,25 +144,29 @@ __global__ __launch_bounds__(kSingleThreads) void layout_single_kernel(LayoutArg
         __syncthreads();
         int32_t before = 0;
         for (int i = 0; i < (tid >> 6); ++i) before += s_tmp[i];
-        if (tid < R) s_off[tid] = before + inc - mine;
+        if (tid < K) s_off[tid] = before + inc - mine;
     }
     __syncthreads();
     for (int32_t d = tid; d < R; d += kSingleThreads) {
-        a.rank_count[d] = s_tot[d];
-        a.recv_offset[d] = s_off[d];
+        a.rank_count[d] = rank_sum(s_tot, d);
+        a.recv_offset[d] = s_off[eord ? d * epr : d];
     }
     if (tid == 0) a.recv_offset[R] = (int32_t)p.rows;
     for (int32_t e = tid; e < E; e += kSingleThreads) a.expert_count[e] = s_eh[e];
+    if (eord && a.expert_offset != nullptr) {
+        for (int32_t e = tid; e < E; e += kSingleThreads) a.expert_offset[e] = s_off[e];
+        if (tid == 0) a.expert_offset[E] = (int32_t)p.rows;
+    }
     // send / chunk offsets are the tile prefixes at source-rank / chunk boundaries
     const int32_t tiles_per_source = (int32_t)(p.tps / p.tile_tokens);
     const int32_t tiles_per_chunk = (int32_t)(p.tpc / p.tile_tokens);
     for (int32_t i = tid; i < R * R; i += kSingleThreads)
-        a.send_offset[i] = s_tc[(i / R) * tiles_per_source * R + i % R];
+        a.send_offset[i] = rank_sum(s_tc + (i / R) * tiles_per_source * K, i % R);
     if (a.chunk_offset != nullptr)
         for (int32_t i = tid; i < p.C * R; i += kSingleThreads)
-            a.chunk_offset[i] = s_tc[(i / R) * tiles_per_chunk * R + i % R];
+            a.chunk_offset[i] = rank_sum(s_tc + (i / R) * tiles_per_chunk * K, i % R);
     __syncthreads();
-    for (int32_t i = tid; i < n_tiles * R; i += kSingleThreads) s_tc[i] += s_off[i % R];
+    for (int32_t i = tid; i < n_tiles * K; i += kSingleThreads) s_tc[i] += s_off[i % K];
     __syncthreads();
 
     // pass 2: stable ranks -> positions (ballot peer masks give the order
@@ -163,10 +177,10 @@ __global__ __launch_bounds__(kSingleThreads) void layout_single_kernel(LayoutArg
         for (int i = 0; i < STEPS; ++i) {
             if (i >= steps) break;                           // uniform across the wave
             const int64_t row = r_lo + 64 * i + lane;
-            const uint32_t d = rank_of((uint32_t)ev[i], p.epr_magic);
-            const uint64_t pd = peers_of_n<8>(d, p.dbits, ~0ull);
+            const uint32_t d = rank_of((uint32_t)ev[i], p.key_magic);
+            const uint64_t pd = peers_of_n<8>(d, p.kbits, ~0ull);
             const uint64_t before = pd & lanemask_lt();
-            const int32_t b = s_tc[tile * R + d];
+            const int32_t b = s_tc[tile * K + d];
             const int32_t q = b + (int32_t)__popcll(before);
             a.pos[row] = q;
             if ((uint32_t)q < (uint32_t)p.rows) {
@@ -174,7 +188,7 @@ __global__ __launch_bounds__(kSingleThreads) void layout_single_kernel(LayoutArg
             } else {
                 bad_pos = true;
             }
-            if (before == 0) s_tc[tile * R + d] = b + (int32_t)__popcll(pd);
+            if (before == 0) s_tc[tile * K + d] = b + (int32_t)__popcll(pd);
             if (++in_tile == steps_per_tile) {
                 in_tile = 0;
                 ++tile;
@@ -183,6 +197,12 @@ __global__ __launch_bounds__(kSingleThreads) void layout_single_kernel(LayoutArg
     }
     if (bad) raise_status(&a.hdr[kHdrStatus], UBEP_ERR_BAD_EXPERT_ID);
     if (bad_pos) raise_status(&a.hdr[kHdrStatus], UBEP_ERR_BAD_POSITION);
+}
+
+// LDS of the persistent layout's workgroup within what a CU offers (the
+// expert order keeps per-wave counts for every expert).
+bool layout_lds_fits(const Plan& p) {
+    return layout_fits_one_group(p) || layout_lds_bytes(p, kLayoutWaves) <= kLdsBytesPerCu;
 }
 
 static std::atomic<int32_t> g_worker_cap{0};
@@ -204,9 +224,9 @@ int64_t layout_workers(const Plan& p, int cus) {
 }
 
 hipError_t launch_layout(const Plan& p, const int32_t* idx, int32_t* pos, int32_t* expert_count,
-                         int32_t* rank_count, int32_t* recv_offset, int32_t* send_offset,
-                         int32_t* chunk_offset, int32_t* recv_src, void* ws, uint64_t spin_ticks,
-                         hipStream_t stream) {
+                         int32_t* expert_offset, int32_t* rank_count, int32_t* recv_offset,
+                         int32_t* send_offset, int32_t* chunk_offset, int32_t* recv_src, void* ws,
+                         uint64_t spin_ticks, hipStream_t stream) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
@@ -222,6 +242,7 @@ hipError_t launch_layout(const Plan& p, const int32_t* idx, int32_t* pos, int32_
     a.send_offset = send_offset;
     a.chunk_offset = p.C > 1 ? chunk_offset : nullptr;
     a.recv_src = recv_src;
+    a.expert_offset = expert_offset;
     char* base = static_cast<char*>(ws);
     a.hdr = reinterpret_cast<uint32_t*>(base);
     a.state = reinterpret_cast<uint64_t*>(base + p.off_state);
@@ -250,10 +271,16 @@ hipError_t launch_layout(const Plan& p, const int32_t* idx, int32_t* pos, int32_
                              (size_t)lds, stream, a);
     };
     static_assert(max_lane_rows<kLayoutWaves>() == 8, "tile rows per lane");
-    if (lane_rows <= 1) return go(layout_kernel<1>);
-    if (lane_rows <= 2) return go(layout_kernel<2>);
-    if (lane_rows <= 4) return go(layout_kernel<4>);
-    return go(layout_kernel<8>);
+    if (p.order != 0) {
+        if (lane_rows <= 1) return go(layout_kernel<1, true>);
+        if (lane_rows <= 2) return go(layout_kernel<2, true>);
+        if (lane_rows <= 4) return go(layout_kernel<4, true>);
+        return go(layout_kernel<8, true>);
+    }
+    if (lane_rows <= 1) return go(layout_kernel<1, false>);
+    if (lane_rows <= 2) return go(layout_kernel<2, false>);
+    if (lane_rows <= 4) return go(layout_kernel<4, false>);
+    return go(layout_kernel<8, false>);
 }
 
 }  // namespace ubep

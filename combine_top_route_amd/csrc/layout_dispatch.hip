@@ -132,8 +132,8 @@ hipError_t launch_layout_dispatch(const Plan& p, const int32_t* idx, const void*
                                   void* recv, void* ws, uint64_t spin_ticks, hipStream_t stream) {
     uint32_t* status = static_cast<uint32_t*>(ws) + kHdrStatus;
     if (!layout_dispatch_fuses(p)) {   // two launches, same result
-        hipError_t e = launch_layout(p, idx, pos, expert_count, rank_count, recv_offset, send_offset,
-                                     chunk_offset, recv_src, ws, spin_ticks, stream);
+        hipError_t e = launch_layout(p, idx, pos, expert_count, nullptr, rank_count, recv_offset,
+                                     send_offset, chunk_offset, recv_src, ws, spin_ticks, stream);
         if (e != hipSuccess) return e;
         return launch_dispatch_bf16(p, x, pos, recv, status, stream);
     }
@@ -152,6 +152,7 @@ hipError_t launch_layout_dispatch(const Plan& p, const int32_t* idx, const void*
     a.send_offset = send_offset;
     a.chunk_offset = p.C > 1 ? chunk_offset : nullptr;
     a.recv_src = recv_src;
+    a.expert_offset = nullptr;
     char* base = static_cast<char*>(ws);
     a.hdr = reinterpret_cast<uint32_t*>(base);
     a.state = reinterpret_cast<uint64_t*>(base + p.off_state);

@@ -8,6 +8,10 @@
 // written and read with agent-scope atomics.  Rows (t, j) are cut into tiles
 // of whole tokens; a tile never straddles a source-rank or chunk boundary.
 // Each tile has R + E "digits": one per destination rank, one per expert.
+// Positions are ranked by "key": the destination rank (rank order) or the
+// expert (expert order, rows grouped by expert inside each region); the key
+// digits are the rank digits or the expert digits.  All per-key arrays below
+// have K = R or K = E entries.
 //
 // Phase A -- the worker takes tiles from a ticket counter, in order, and
 //   claims its next tile while it works on the current one:
@@ -51,25 +55,26 @@ struct LayoutArgs {
     int32_t* send_offset;
     int32_t* chunk_offset;   // may be null
     int32_t* recv_src;       // may be null
+    int32_t* expert_offset;  // [E+1], expert order only (may be null)
     uint32_t* hdr;
     uint64_t* state;         // [n_tiles][R + E]
-    int32_t* excl;           // [n_tiles][R]
-    int32_t* wbase;          // [n_tiles][NW][R]
+    int32_t* excl;           // [n_tiles][K]
+    int32_t* wbase;          // [n_tiles][NW][K]
     Plan p;
     uint64_t spin_ticks;
 };
 
 // LDS of one worker, carved from the kernel's dynamic shared memory.
 struct LayoutLds {
-    int32_t* wh;      // [NW][R] per-wave rank counts, then running bases
+    int32_t* wh;      // [NW][K] per-wave key counts, then running bases
     int32_t* eh;      // [E]     tile expert counts
-    int32_t* cnt;     // [R]     tile rank counts, then rank totals
-    int32_t* excl;    // [R]     rows to rank d before the last claimed tile
-    int32_t* off;     // [R]     recv_offset
+    int32_t* cnt;     // [K]     tile key counts, then key totals
+    int32_t* excl;    // [K]     rows with key q before the last claimed tile
+    int32_t* off;     // [K]     exclusive scan of the key totals
     uint32_t* tiles;  // [kMaxTilesPerGroup] tiles this workgroup claimed
     int32_t* tmp;     // [NW]
     uint32_t* ticket; // [1]
-    int32_t* bins;    // gather mode: [kGatherMaxMine + 1][R] rank counts binned by own tiles
+    int32_t* bins;    // gather mode: [kGatherMaxMine + 1][K] key counts binned by own tiles
 };
 
 // Tiles one worker may claim.
@@ -78,18 +83,18 @@ __host__ __device__ inline int64_t layout_claim_limit(const Plan& p) {
 }
 
 inline int64_t layout_lds_bytes(const Plan& p, int nw) {
-    const int64_t bins = p.gather ? (int64_t)(kGatherMaxMine + 1) * p.R : 0;
-    return 4 * ((int64_t)nw * p.R + p.E + 3 * (int64_t)p.R + kMaxTilesPerGroup + nw + 1 + bins);
+    const int64_t bins = p.gather ? (int64_t)(kGatherMaxMine + 1) * p.K : 0;
+    return 4 * ((int64_t)nw * p.K + p.E + 3 * (int64_t)p.K + kMaxTilesPerGroup + nw + 1 + bins);
 }
 
 __device__ __forceinline__ LayoutLds carve_lds(int32_t* base, const Plan& p, int nw) {
     LayoutLds L;
     L.wh = base;
-    L.eh = L.wh + nw * p.R;
+    L.eh = L.wh + nw * p.K;
     L.cnt = L.eh + p.E;
-    L.excl = L.cnt + p.R;
-    L.off = L.excl + p.R;
-    L.tiles = reinterpret_cast<uint32_t*>(L.off + p.R);
+    L.excl = L.cnt + p.K;
+    L.off = L.excl + p.K;
+    L.tiles = reinterpret_cast<uint32_t*>(L.off + p.K);
     L.tmp = reinterpret_cast<int32_t*>(L.tiles + kMaxTilesPerGroup);
     L.ticket = reinterpret_cast<uint32_t*>(L.tmp + nw);
     L.bins = reinterpret_cast<int32_t*>(L.ticket + 1);
@@ -141,10 +146,11 @@ __device__ __forceinline__ void check_ids(const Plan& p, int32_t (&ev)[LR], bool
     }
 }
 
-// wh[w*R + d] = rows of wave w with rank d; eh[e] = rows of the tile with
-// expert e.  Counting needs no order, so plain LDS atomics do it (a hot key
+// wh[w*K + q] = rows of wave w with key q; eh[e] = rows of the tile with
+// expert e (rank order only: in expert order the key counts are the expert
+// counts).  Counting needs no order, so plain LDS atomics do it (a hot key
 // under skew only serialises its own lanes).
-template <int NW, int LR>
+template <int NW, int LR, bool EORD>
 __device__ __forceinline__ void tile_histograms(const Plan& p, const int32_t (&ev)[LR],
                                                 int32_t* wh, int32_t* eh) {
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -155,17 +161,17 @@ __device__ __forceinline__ void tile_histograms(const Plan& p, const int32_t (&e
         if (lo + 64 * i >= hi) break;                      // uniform across the wave
         if (lo + 64 * i + lane < hi) {
             const uint32_t e = (uint32_t)ev[i];
-            atomicAdd(&wh[w * p.R + rank_of(e, p.epr_magic)], 1);
-            atomicAdd(&eh[e], 1);
+            atomicAdd(&wh[w * (EORD ? p.K : p.R) + (EORD ? e : rank_of(e, p.epr_magic))], 1);
+            if constexpr (!EORD) atomicAdd(&eh[e], 1);
         }
     }
 }
 
-// Stable ranking inside a tile: base[w*R + d] holds the value of wave w's
-// first row with rank d; every row gets base + (rows before it in the wave
-// with rank d), and base advances.  Ballot peer masks give the order among
+// Stable ranking inside a tile: base[w*K + q] holds the value of wave w's
+// first row with key q; every row gets base + (rows before it in the wave
+// with key q), and base advances.  Ballot peer masks give the order among
 // equal ranks inside a 64-row step; steps run in row order.
-template <int NW, int LR>
+template <int NW, int LR, bool EORD>
 __device__ __forceinline__ void tile_ranks(const Plan& p, const int32_t (&ev)[LR],
                                            int32_t* base, int32_t (&rank)[LR]) {
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -176,13 +182,14 @@ __device__ __forceinline__ void tile_ranks(const Plan& p, const int32_t (&ev)[LR
         rank[i] = 0;
         if (lo + 64 * i >= hi) continue;                   // uniform across the wave
         const bool act = lo + 64 * i + lane < hi;
-        const uint32_t d = rank_of((uint32_t)ev[i], p.epr_magic);
-        const uint64_t pd = peers_of_n<10>(d, p.dbits, __ballot(act));
+        const uint32_t d = EORD ? (uint32_t)ev[i] : rank_of((uint32_t)ev[i], p.epr_magic);
+        const uint64_t pd = peers_of_n<EORD ? 13 : 10>(d, EORD ? p.ebits : p.dbits, __ballot(act));
         const uint64_t before = pd & lanemask_lt();
         if (act) {
-            const int32_t b = base[w * p.R + d];
+            const int32_t K = EORD ? p.K : p.R;
+            const int32_t b = base[w * K + d];
             rank[i] = b + (int32_t)__popcll(before);
-            if (before == 0) base[w * p.R + d] = b + (int32_t)__popcll(pd);
+            if (before == 0) base[w * K + d] = b + (int32_t)__popcll(pd);
         }
     }
 }
@@ -343,7 +350,7 @@ __device__ __forceinline__ void gather_aggregates(const LayoutArgs& a, int32_t c
 // it has its totals -- its last ticket claim has returned long before, and it
 // touches no ticket, counter or epoch word after that -- and receives the
 // counter's old value (its round trip overlaps the scan and the stores).
-template <int NW, int LR, bool COH_POS, int W = kLookbackWindow>
+template <int NW, int LR, bool COH_POS, int W = kLookbackWindow, bool EORD = false>
 __device__ __forceinline__ void layout_worker(const LayoutArgs& a, const LayoutLds& L, uint32_t epoch,
                                               uint32_t wid, uint32_t nw_workers,
                                               uint32_t* done = nullptr) {
@@ -351,7 +358,9 @@ __device__ __forceinline__ void layout_worker(const LayoutArgs& a, const LayoutL
     constexpr int T_ = NW * 64;
     const Plan& p = a.p;
     const int tid = threadIdx.x;
-    const int32_t R = p.R, E = p.E, S = p.slots;
+    constexpr bool eord = EORD;   // expert order (p.order == 1)
+    const int32_t R = p.R, E = p.E, S = p.slots, epr = p.epr;
+    const int32_t K = eord ? p.K : p.R, kcol = eord ? p.kcol : 0;
     bool bad = false, bad_pos = false, timed_out = false;
     uint32_t n_mine = 0;
     int32_t ev[LR];                                  // ids of the last claimed tile
@@ -370,8 +379,9 @@ __device__ __forceinline__ void layout_worker(const LayoutArgs& a, const LayoutL
     if (wid < (uint64_t)p.n_tiles) load_ids<NW, LR>(a, wid, nv);
     for (;;) {
         if (tid == 0) *L.ticket = claim;
-        for (int i = tid; i < NW * R; i += T_) L.wh[i] = 0;
-        for (int i = tid; i < E; i += T_) L.eh[i] = 0;
+        for (int i = tid; i < NW * K; i += T_) L.wh[i] = 0;
+        if (!eord)
+            for (int i = tid; i < E; i += T_) L.eh[i] = 0;
         __syncthreads();
         const uint32_t tile = *L.ticket;
         if (tile >= (uint64_t)p.n_tiles) break;
@@ -381,7 +391,7 @@ __device__ __forceinline__ void layout_worker(const LayoutArgs& a, const LayoutL
         check_ids<NW, LR>(p, ev, &bad);
         if (tid == 0) L.tiles[n_mine] = tile;
         ++n_mine;
-        tile_histograms<NW, LR>(p, ev, L.wh, L.eh);
+        tile_histograms<NW, LR, EORD>(p, ev, L.wh, L.eh);
         __syncthreads();
         // claim the next tile now, after the barrier (so that the ids are in
         // registers: a claim issued before they arrived would be waited on
@@ -390,35 +400,46 @@ __device__ __forceinline__ void layout_worker(const LayoutArgs& a, const LayoutL
         if (tid == 0) claim = n_mine < cap ? add_relaxed(&a.hdr[kHdrLayoutTicket], 1u) : 0xFFFFFFFFu;
 
         // wave bases (kept for a later re-rank), tile aggregates, publish
-        int32_t* wb = a.wbase + (int64_t)tile * NW * R;
-        for (int32_t d = tid; d < R; d += T_) {
+        int32_t* wb = a.wbase + (int64_t)tile * NW * K;
+        for (int32_t d = tid; d < K; d += T_) {
             int32_t run = 0;
 #pragma unroll
             for (int v = 0; v < NW; ++v) {
-                const int32_t c = L.wh[v * R + d];
-                L.wh[v * R + d] = run;
-                wb[v * R + d] = run;
+                const int32_t c = L.wh[v * K + d];
+                L.wh[v * K + d] = run;
+                wb[v * K + d] = run;
                 run += c;
             }
             L.cnt[d] = run;
         }
         __syncthreads();
+        // the tile's count of digit s: a rank (s < R) or an expert
+        const auto digit_count = [&](int32_t s) -> int32_t {
+            if (!eord) return s < R ? L.cnt[s] : L.eh[s - R];
+            if (s >= R) return L.cnt[s - R];
+            int32_t c = 0;
+            for (int32_t e = s * epr; e < (s + 1) * epr; ++e) c += L.cnt[e];
+            return c;
+        };
         uint64_t* st = a.state + (int64_t)tile * S;
         for (int32_t s = tid; s < S; s += T_) {
-            const int32_t c = s < R ? L.cnt[s] : L.eh[s - R];
+            const int32_t c = digit_count(s);
             st_relaxed64(st + s, state_word(epoch, tile == 0 ? kFlagInclusive : kFlagAggregate, c));
         }
         // in-tile ranks now, while the other tiles publish
-        tile_ranks<NW, LR>(p, ev, L.wh, lrank);
+        tile_ranks<NW, LR, EORD>(p, ev, L.wh, lrank);
         if (!gather) {
             const int64_t tok0 = (int64_t)tile * p.tile_tokens;
             for (int32_t s = tid; s < S; s += T_) {
-                const int32_t c = s < R ? L.cnt[s] : L.eh[s - R];
+                const int32_t c = digit_count(s);
                 const int32_t excl = tile == 0 ? 0 : look_back<W>(a, tile, s, epoch, &timed_out);
                 if (tile != 0) st_relaxed64(st + s, state_word(epoch, kFlagInclusive, excl + c));
+                const int32_t q = s - kcol;
+                if ((uint32_t)q < (uint32_t)K) {
+                    L.excl[q] = excl;
+                    a.excl[(int64_t)tile * K + q] = excl;
+                }
                 if (s < R) {
-                    L.excl[s] = excl;
-                    a.excl[(int64_t)tile * R + s] = excl;
                     if (tok0 % p.tps == 0) a.send_offset[(tok0 / p.tps) * R + s] = excl;
                     if (a.chunk_offset != nullptr && tok0 % p.tpc == 0)
                         a.chunk_offset[(tok0 / p.tpc) * R + s] = excl;
@@ -437,42 +458,44 @@ __device__ __forceinline__ void layout_worker(const LayoutArgs& a, const LayoutL
         // fewer than m + 1 of them are at or before j, so the running sum
         // over b up to m is the exclusive prefix of tiles[m], and up to
         // n_mine the total.
-        for (int i = tid; i < (n_m + 1) * R; i += T_) L.bins[i] = 0;
-        const int32_t e_per = (E + (int32_t)nw_workers - 1) / (int32_t)nw_workers;
-        e_lo = (int64_t)wid * e_per < E ? (int32_t)wid * e_per : E;
-        n_e = E - e_lo < e_per ? E - e_lo : e_per;
+        for (int i = tid; i < (n_m + 1) * K; i += T_) L.bins[i] = 0;
+        if (!eord) {   // in expert order the key totals are the expert counts
+            const int32_t e_per = (E + (int32_t)nw_workers - 1) / (int32_t)nw_workers;
+            e_lo = (int64_t)wid * e_per < E ? (int32_t)wid * e_per : E;
+            n_e = E - e_lo < e_per ? E - e_lo : e_per;
+        }
         for (int i = tid; i < n_e; i += T_) L.eh[i] = 0;
         __syncthreads();
-        gather_aggregates<T_>(a, 0, R, epoch, &timed_out, [&](int32_t j, int32_t d, int32_t c) {
+        gather_aggregates<T_>(a, kcol, K, epoch, &timed_out, [&](int32_t j, int32_t d, int32_t c) {
             int32_t b = 0;
             for (int32_t m = 0; m < n_m; ++m) b += (int32_t)L.tiles[m] <= j ? 1 : 0;
-            atomicAdd(&L.bins[b * R + d], c);
+            atomicAdd(&L.bins[b * K + d], c);
         });
         if (n_e > 0)
             gather_aggregates<T_>(a, R + e_lo, n_e, epoch, &timed_out,
                                   [&](int32_t, int32_t e, int32_t c) { atomicAdd(&L.eh[e], c); });
         __syncthreads();
-        for (int32_t d = tid; d < R; d += T_) {
+        for (int32_t d = tid; d < K; d += T_) {
             int32_t run = 0;
             for (int32_t m = 0; m <= n_m; ++m) {
-                run += L.bins[m * R + d];
-                L.bins[m * R + d] = run;   // prefix of tiles[m] (m < n_mine), total (m = n_mine)
+                run += L.bins[m * K + d];
+                L.bins[m * K + d] = run;   // prefix of tiles[m] (m < n_mine), total (m = n_mine)
             }
             L.cnt[d] = run;
-            if (n_m > 0) L.excl[d] = L.bins[(n_m - 1) * R + d];
+            if (n_m > 0) L.excl[d] = L.bins[(n_m - 1) * K + d];
         }
     } else {
-        for (int32_t d = tid; d < R; d += T_) L.cnt[d] = wait_total(a, d, epoch, &timed_out);
+        for (int32_t d = tid; d < K; d += T_) L.cnt[d] = wait_total(a, kcol + d, epoch, &timed_out);
     }
     // this workgroup touches no ticket, counter or epoch word from here on
     if (done != nullptr && tid == 0) *done = add_relaxed(&a.hdr[kHdrLayoutDone], 1u);
     __syncthreads();
-    {   // exclusive scan of the rank totals; thread i owns a run of ranks
-        const int per = (R + T_ - 1) / T_;
+    {   // exclusive scan of the key totals; thread i owns a run of keys
+        const int per = (K + T_ - 1) / T_;
         int32_t mine = 0;
         for (int i = 0; i < per; ++i) {
             const int32_t d = tid * per + i;
-            if (d < R) mine += L.cnt[d];
+            if (d < K) mine += L.cnt[d];
         }
         const int lane = tid & 63, w = tid >> 6;
         int32_t inc = mine;
@@ -487,7 +510,7 @@ __device__ __forceinline__ void layout_worker(const LayoutArgs& a, const LayoutL
         for (int i = 0; i < w; ++i) run += L.tmp[i];
         for (int i = 0; i < per; ++i) {
             const int32_t d = tid * per + i;
-            if (d < R) {
+            if (d < K) {
                 L.off[d] = run;
                 run += L.cnt[d];
             }
@@ -500,7 +523,7 @@ __device__ __forceinline__ void layout_worker(const LayoutArgs& a, const LayoutL
         if (m + 1 == n_mine) {     // the last claimed tile: ids and in-tile ranks in registers
 #pragma unroll
             for (int i = 0; i < LR; ++i) {
-                const uint32_t d = rank_of((uint32_t)ev[i], p.epr_magic);
+                const uint32_t d = eord ? (uint32_t)ev[i] : rank_of((uint32_t)ev[i], p.epr_magic);
                 q[i] = L.off[d] + L.excl[d] + lrank[i];
             }
         } else {                   // an earlier tile of this workgroup: rebuild from its state
@@ -509,38 +532,52 @@ __device__ __forceinline__ void layout_worker(const LayoutArgs& a, const LayoutL
             bool ignore = false;
             check_ids<NW, LR>(p, ids, &ignore);
             __syncthreads();
-            for (int i = tid; i < NW * R; i += T_) {
-                const int32_t d = i % R;
-                const int32_t excl = gather ? L.bins[m * R + d] : a.excl[tile * R + d];
-                L.wh[i] = L.off[d] + excl + a.wbase[tile * NW * R + i];
+            for (int i = tid; i < NW * K; i += T_) {
+                const int32_t d = i % K;
+                const int32_t excl = gather ? L.bins[m * K + d] : a.excl[tile * K + d];
+                L.wh[i] = L.off[d] + excl + a.wbase[tile * NW * K + i];
             }
             __syncthreads();
-            tile_ranks<NW, LR>(p, ids, L.wh, q);
+            tile_ranks<NW, LR, EORD>(p, ids, L.wh, q);
         }
         store_positions<NW, LR, COH_POS>(a, tile, q, &bad_pos);
     }
 
     // outputs that nothing in this kernel reads, stored last so that no wait
     // above covers them
+    // rows with a key of rank d in a per-key array v (rank order: v[d])
+    const auto rank_sum = [&](const int32_t* v, int32_t d) -> int32_t {
+        if (!eord) return v[d];
+        int32_t c = 0;
+        for (int32_t e = d * epr; e < (d + 1) * epr; ++e) c += v[e];
+        return c;
+    };
     if (gather) {
         for (int32_t d = tid; d < R; d += T_) {
             for (int32_t m = 0; m < n_m; ++m) {
                 const int64_t tok0 = (int64_t)L.tiles[m] * p.tile_tokens;
-                if (tok0 % p.tps == 0) a.send_offset[(tok0 / p.tps) * R + d] = L.bins[m * R + d];
+                if (tok0 % p.tps == 0) a.send_offset[(tok0 / p.tps) * R + d] = rank_sum(L.bins + m * K, d);
                 if (a.chunk_offset != nullptr && tok0 % p.tpc == 0)
-                    a.chunk_offset[(tok0 / p.tpc) * R + d] = L.bins[m * R + d];
+                    a.chunk_offset[(tok0 / p.tpc) * R + d] = rank_sum(L.bins + m * K, d);
             }
         }
         for (int i = tid; i < n_e; i += T_) a.expert_count[e_lo + i] = L.eh[i];
-    } else if (leader) {
+    } else if (leader && !eord) {
         for (int32_t e = tid; e < E; e += T_) a.expert_count[e] = wait_total(a, R + e, epoch, &timed_out);
     }
     if (leader) {
         for (int32_t d = tid; d < R; d += T_) {
-            a.rank_count[d] = L.cnt[d];
-            a.recv_offset[d] = L.off[d];
+            a.rank_count[d] = rank_sum(L.cnt, d);
+            a.recv_offset[d] = L.off[eord ? d * epr : d];
         }
-        if (tid == 0) a.recv_offset[R] = L.off[R - 1] + L.cnt[R - 1];
+        if (tid == 0) a.recv_offset[R] = L.off[K - 1] + L.cnt[K - 1];
+        if (eord) {    // key totals and their scan are the expert counts and offsets
+            for (int32_t e = tid; e < E; e += T_) {
+                a.expert_count[e] = L.cnt[e];
+                if (a.expert_offset != nullptr) a.expert_offset[e] = L.off[e];
+            }
+            if (tid == 0 && a.expert_offset != nullptr) a.expert_offset[E] = L.off[E - 1] + L.cnt[E - 1];
+        }
     }
 
     if (bad) raise_status(&a.hdr[kHdrStatus], UBEP_ERR_BAD_EXPERT_ID);

@@ -21,6 +21,7 @@ constexpr int kGateMaxGroups = 64;
 constexpr int kLayoutThreads = 512;
 constexpr int kLayoutWaves = 8;
 constexpr int64_t kTileRowsMax = 4096;
+constexpr int64_t kLdsBytesPerCu = 160 * 1024;
 
 // Workspace header: 32-bit counters, each on its own 128-byte line.
 constexpr int kHdrStatus = 0;          // device status word (ubep_status)
@@ -48,7 +49,7 @@ constexpr int kLookbackWindow = 32;              // predecessor states read per 
 constexpr int kMaxTilesPerGroup = 256;           // tiles one layout workgroup may claim
 // Gather mode (few tiles): every worker sums all tiles' published counts
 // instead of looking back; a worker then claims at most kGatherMaxMine tiles.
-constexpr int64_t kGatherMaxWords = 16384;       // n_tiles * R
+constexpr int64_t kGatherMaxWords = 16384;       // n_tiles * K
 constexpr int64_t kGatherMaxTiles = 512;
 constexpr int kGatherMaxMine = 8;
 constexpr int kGatherBurst = 8;                  // state words a thread loads at once
@@ -68,16 +69,26 @@ struct Plan {
     int32_t dbits;         // bits to hold a rank id (0..R-1)
     int32_t ebits;         // bits to hold an expert id (0..E-1)
     int32_t gather;        // 1: prefixes and totals by gathering all tiles' counts
+    // Position keys.  Rank order: rows sort by (rank, token, slot), one key per
+    // rank.  Expert order: rows sort by (expert, token, slot), one key per
+    // expert (a rank's experts are consecutive, so its region is still one
+    // run).  key(e) = rank_of(e, key_magic).
+    int32_t order;         // 0: rank order, 1: expert order
+    int32_t K;             // keys: R or E
+    uint32_t key_magic;    // epr_magic (rank order) or 0 (expert order: key = e)
+    int32_t kbits;         // bits to hold a key
+    int32_t kcol;          // state digit of key 0: 0 (rank digits) or R (expert digits)
     // workspace byte offsets
     int32_t slots;         // look-back digits per tile: R ranks, then E experts
     size_t off_state;      // uint64 [n_tiles][R+E]  look-back state
-    size_t off_excl;       // int32  [n_tiles][R]    rows to rank d in earlier tiles
-    size_t off_wbase;      // int32  [n_tiles][8][R] rows to rank d in earlier waves of the tile
+    size_t off_excl;       // int32  [n_tiles][K]    rows with key q in earlier tiles (sized for K = E)
+    size_t off_wbase;      // int32  [n_tiles][8][K] rows with key q in earlier waves of the tile
     size_t off_flags;      // uint32 [C][kFlagStride] chunk ready flags
     size_t ws_bytes;
 };
 
-// Host: fill `p` for a shape that passed validation.
-void make_plan(const ubep_shape& s, Plan* p);
+// Host: fill `p` for a shape that passed validation; order 0 (rank order)
+// or 1 (expert order).  The workspace layout does not depend on the order.
+void make_plan(const ubep_shape& s, Plan* p, int order = 0);
 
 }  // namespace ubep

@@ -130,6 +130,36 @@ ubep_status ubep_layout(const ubep_shape *shape /*host*/, const int32_t *topk_id
                         int32_t *recv_offset, int32_t *send_offset, int32_t *chunk_offset,
                         int32_t *recv_src, void *ws, size_t ws_bytes, hipStream_t stream);
 
+/* Expert-grouped layout: the same call as ubep_layout, except that inside
+ * each rank's region the rows are ordered by (expert, token, slot), so every
+ * expert's rows form one contiguous run -- the order a grouped per-expert
+ * computation between dispatch and combine reads.  (The UBEP page fixes only
+ * that each token reaches the device of each expert it selected and comes
+ * back, opening section; the order inside a region is this library's.)
+ * Outputs (int32, fully overwritten):
+ *   pos[T][k]          expert_offset[e] + number of rows (t', j') < (t, j)
+ *                      in (token, slot) order with the same expert
+ *                      e = topk_idx[t][j];
+ *   expert_count[E]    rows per expert;
+ *   expert_offset[E+1] exclusive prefix sum of expert_count; [E] = T*k;
+ *   rank_count[R], recv_offset[R+1]  as ubep_layout (recv_offset[d] =
+ *                      expert_offset[d * E/R]: a rank's experts are
+ *                      consecutive ids, so region d is the run of its experts);
+ *   send_offset[R][R], chunk_offset[C][R]  the same row counts as ubep_layout
+ *                      (rows to rank d from earlier source ranks / chunks);
+ *                      in this order they are counts, not start rows;
+ *   recv_src[T*k]      inverse of pos (may be NULL).
+ * The workspace is the one ubep_workspace_bytes sizes (shared with every
+ * other call).  Bad ids: as ubep_layout.  UBEP_ERR_UNSUPPORTED when the
+ * per-expert counts of one layout workgroup exceed a CU's 160 KB of LDS
+ * (E above about 2048).  dispatch, combine and the chunk
+ * pipeline take this pos unchanged.  One kernel on `stream`. */
+ubep_status ubep_layout_grouped(const ubep_shape *shape /*host*/, const int32_t *topk_idx,
+                                int32_t *pos, int32_t *expert_count, int32_t *expert_offset,
+                                int32_t *rank_count, int32_t *recv_offset, int32_t *send_offset,
+                                int32_t *chunk_offset, int32_t *recv_src, void *ws,
+                                size_t ws_bytes, hipStream_t stream);
+
 /* Layout and bf16 dispatch in one launch ("Kernel Decomposition": a few
  * workgroups compute the layout and publish it to global memory while the
  * others load their token rows and poll for it, instead of a barrier between

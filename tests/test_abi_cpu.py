@@ -120,3 +120,18 @@ def test_gate_validation_without_gpu():
             ubep.ubep_gate(c["T"], c["E"], c["k"], p, p, p, c.get("groups", 1), c.get("keep_groups", 1), 0,
                            stream=0)
         assert e.value.code == ubep.ERR_UNSUPPORTED, c
+
+
+def test_grouped_layout_validation_without_gpu():
+    """ubep_layout_grouped: null outputs and LDS-exceeding expert counts fail on
+    the host (dummy pointers are never used)."""
+    L = ubep.lib()
+    s = ubep.ubep_shape(8, 64, 4, 2, 2, 1)
+    nws = L.ubep_workspace_bytes(C.byref(s))
+    assert L.ubep_layout_grouped(C.byref(s), 256, 256, 256, None, 256, 256, 256, None, None, 256,
+                                 nws, None) == ubep.ERR_INVALID_ARG        # no expert_offset
+    big = ubep.ubep_shape(8192, 64, 8192, 2, 1, 1)                          # 8192 experts
+    nws = L.ubep_workspace_bytes(C.byref(big))
+    assert nws > 0
+    assert L.ubep_layout_grouped(C.byref(big), 256, 256, 256, 256, 256, 256, 256, None, None, 256,
+                                 nws, None) == ubep.ERR_UNSUPPORTED
