@@ -194,9 +194,12 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=None, help="workload name (default: DeepSeek-V3 decode)")
-    ap.add_argument("--mode", choices=["unfused", "chunked", "gated", "fused"], default="unfused",
+    ap.add_argument("--mode", choices=["unfused", "chunked", "sentinel", "gated", "fused"],
+                    default="unfused",
                     help="gated: the step starts from router logits (ubep_gate, then unfused); "
-                         "fused: ubep_layout_dispatch (one launch), then combine")
+                         "fused: ubep_layout_dispatch (one launch), then combine; "
+                         "sentinel: layout, then ubep_dispatch_combine_sentinel (token-granular "
+                         "readiness polled in the rows)")
     ap.add_argument("--order", choices=["rank", "expert"], default="rank",
                     help="receive order inside a rank's region: (token, slot) with ubep_layout, or "
                          "expert-grouped (expert, token, slot) with ubep_layout_grouped")
@@ -233,8 +236,8 @@ def main(argv=None):
     sd = s.as_dict()
     fp8 = w.recipe.payload == "fp8"
     dtype = ubep.FP8_E4M3 if fp8 else ubep.BF16
-    if args.mode == "chunked" and fp8:
-        print("the chunk pipeline carries a bf16 payload only", file=sys.stderr)
+    if args.mode in ("chunked", "sentinel") and fp8:
+        print("the pipelined kernels carry a bf16 payload only", file=sys.stderr)
         return 2
     if args.mode == "fused" and args.order == "expert":
         print("the fused launch computes the rank-order layout only", file=sys.stderr)
@@ -250,7 +253,10 @@ def main(argv=None):
     # step pays to write back)
     scrub = torch.ones(512 << 20, dtype=torch.uint8, device="cuda").view(torch.int64)
 
-    calls = ["layout"] + (["chunked"] if args.mode == "chunked" else ["dispatch", "combine"])
+    calls = ["layout"] + ([args.mode] if args.mode in ("chunked", "sentinel")
+                          else ["dispatch", "combine"])
+    if args.mode == "sentinel":
+        ubep.ubep_recv_sentinel_init(b.recv, s.T * s.k, s.H)
     if args.mode == "fused":
         if fp8:
             print("the fused launch carries a bf16 payload only", file=sys.stderr)
@@ -280,6 +286,9 @@ def main(argv=None):
             ubep.ubep_layout_dispatch(sd, b.topk_idx, b.x, b.pos, b.expert_count, b.rank_count,
                                       b.recv_offset, b.send_offset, chunk_off, None, b.recv, b.ws,
                                       stream)
+        elif name == "sentinel":
+            ubep.ubep_dispatch_combine_sentinel(sd, b.x, b.pos, b.topk_w, b.recv, b.out, b.ws,
+                                                stream=stream)
         elif name == "chunked":
             ubep.ubep_dispatch_combine_chunked(sd, b.x, b.pos, b.topk_w, b.recv, b.out, None,
                                                b.ws, stream=stream)
@@ -436,7 +445,7 @@ def main(argv=None):
 
     nb = algorithmic_bytes(sd, fp8, gated)
     gbs = nb["total"] / (ms * 1e-3) / 1e9
-    dom_bytes = nb["dispatch"] + nb["combine"] if dom == "chunked" else nb[dom]
+    dom_bytes = nb["dispatch"] + nb["combine"] if dom in ("chunked", "sentinel") else nb[dom]
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
     traffic = read_counters(dom, name)
 

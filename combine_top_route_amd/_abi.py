@@ -20,10 +20,12 @@ ERR_TIMEOUT = 4
 ERR_HIP = 5
 ERR_BAD_POSITION = 6
 ERR_WORKSPACE = 7
+ERR_SENTINEL_DATA = 8
 STATUS_NAMES = {OK: "UBEP_OK", ERR_INVALID_ARG: "UBEP_ERR_INVALID_ARG",
                 ERR_UNSUPPORTED: "UBEP_ERR_UNSUPPORTED", ERR_BAD_EXPERT_ID: "UBEP_ERR_BAD_EXPERT_ID",
                 ERR_TIMEOUT: "UBEP_ERR_TIMEOUT", ERR_HIP: "UBEP_ERR_HIP",
-                ERR_BAD_POSITION: "UBEP_ERR_BAD_POSITION", ERR_WORKSPACE: "UBEP_ERR_WORKSPACE"}
+                ERR_BAD_POSITION: "UBEP_ERR_BAD_POSITION", ERR_WORKSPACE: "UBEP_ERR_WORKSPACE",
+                ERR_SENTINEL_DATA: "UBEP_ERR_SENTINEL_DATA"}
 
 BF16 = 0
 FP8_E4M3 = 1
@@ -75,6 +77,8 @@ def lib() -> C.CDLL:
             "ubep_dispatch": ([S, C.c_int, P, P, P, P, P, SZ, P], C.c_int),
             "ubep_combine": ([S, P, P, P, P, P, SZ, P], C.c_int),
             "ubep_dispatch_combine_chunked": ([S, P, P, P, P, P, P, U64, U32, P, SZ, P], C.c_int),
+            "ubep_dispatch_combine_sentinel": ([S, P, P, P, P, P, U64, U32, P, SZ, P], C.c_int),
+            "ubep_recv_sentinel_init": ([P, I64, I64, P], C.c_int),
             "ubep_get_device_status": ([P, SZ, P, C.POINTER(C.c_int)], C.c_int),
             "ubep_identity_expert_fp8": ([I64, I64, P, P, P, P], C.c_int),
             "ubep_copy": ([P, P, SZ, P], C.c_int),
@@ -202,6 +206,19 @@ def ubep_dispatch_combine_chunked(shape, x, pos, topk_w, recv, out, chunk_order,
         C.byref(s), _ptr(x), _ptr(pos), _ptr(topk_w), _ptr(recv), _ptr(out),
         C.cast(order, C.c_void_p) if order is not None else None, spin_limit_ns, debug_flags,
         _ptr(ws), _nbytes(ws), _stream(stream)), "ubep_dispatch_combine_chunked")
+
+
+def ubep_dispatch_combine_sentinel(shape, x, pos, topk_w, recv, out, ws, spin_limit_ns: int = 0,
+                                   debug_flags: int = 0, stream=None):
+    s = _shape(shape)
+    _check(lib().ubep_dispatch_combine_sentinel(
+        C.byref(s), _ptr(x), _ptr(pos), _ptr(topk_w), _ptr(recv), _ptr(out), spin_limit_ns,
+        debug_flags, _ptr(ws), _nbytes(ws), _stream(stream)), "ubep_dispatch_combine_sentinel")
+
+
+def ubep_recv_sentinel_init(recv, rows, H, stream=None):
+    _check(lib().ubep_recv_sentinel_init(_ptr(recv), rows, H, _stream(stream)),
+           "ubep_recv_sentinel_init")
 
 
 def ubep_get_device_status(ws, stream=None) -> int:

@@ -125,6 +125,7 @@ const char* ubep_status_str(ubep_status s) {
         case UBEP_ERR_HIP: return "HIP runtime error";
         case UBEP_ERR_BAD_POSITION: return "position outside [0, T*k)";
         case UBEP_ERR_WORKSPACE: return "workspace counters inconsistent; re-initialize the workspace";
+        case UBEP_ERR_SENTINEL_DATA: return "input row holds the readiness sentinel word";
     }
     return "unknown status";
 }
@@ -287,6 +288,33 @@ ubep_status ubep_dispatch_combine_chunked(const ubep_shape* s, const void* x, co
     if (hipGetDevice(&dev) != hipSuccess) return UBEP_ERR_HIP;
     return hip_status(launch_chunked(p, x, pos, topk_w, recv, out, chunk_order, ticks, debug_flags,
                                      ws, dev, stream));
+}
+
+ubep_status ubep_dispatch_combine_sentinel(const ubep_shape* s, const void* x, const int32_t* pos,
+                                           const float* topk_w, void* recv, void* out,
+                                           uint64_t spin_limit_ns, uint32_t debug_flags, void* ws,
+                                           size_t ws_bytes, hipStream_t stream) {
+    Plan p;
+    const ubep_status st = check_and_plan(s, UBEP_BF16, &p);
+    if (st != UBEP_OK) return st;
+    if (!x || !pos || !topk_w || !recv || !out || !ws || ws_bytes < kHdrBytes) return UBEP_ERR_INVALID_ARG;
+    if (!aligned(x, 16) || !aligned(recv, 16) || !aligned(out, 16) || !aligned(ws, 256))
+        return UBEP_ERR_INVALID_ARG;
+    if (debug_flags & ~1u) return UBEP_ERR_INVALID_ARG;
+    uint64_t ticks;
+    const ubep_status ts = spin_ticks_for(spin_limit_ns, &ticks);
+    if (ts != UBEP_OK) return ts;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return UBEP_ERR_HIP;
+    return hip_status(launch_sentinel_pipeline(p, x, pos, topk_w, recv, out, ticks, debug_flags, ws,
+                                               dev, stream));
+}
+
+ubep_status ubep_recv_sentinel_init(void* recv, int64_t rows, int64_t H, hipStream_t stream) {
+    if (!recv || rows < 0 || H <= 0 || H % 8 != 0 || !aligned(recv, 16)) return UBEP_ERR_INVALID_ARG;
+    if (rows == 0) return UBEP_OK;
+    if (rows >= ((int64_t)1 << 40)) return UBEP_ERR_UNSUPPORTED;
+    return hip_status(launch_sentinel_fill(recv, rows, H, stream));
 }
 
 ubep_status ubep_get_device_status(void* ws, size_t ws_bytes, hipStream_t stream,

@@ -71,6 +71,11 @@ hipError_t launch_chunked(const Plan& p, const void* x, const int32_t* pos, cons
 hipError_t launch_gate(const ubep_gate_shape& g, const float* logits, int32_t* idx, float* w,
                        hipStream_t stream);
 
+hipError_t launch_sentinel_pipeline(const Plan& p, const void* x, const int32_t* pos,
+                                    const float* topk_w, void* recv, void* out, uint64_t spin_ticks,
+                                    uint32_t debug_flags, void* ws, int device, hipStream_t stream);
+hipError_t launch_sentinel_fill(void* recv, int64_t rows, int64_t H, hipStream_t stream);
+
 hipError_t launch_identity_fp8(int64_t rows, int64_t H, const uint8_t* q, const float* scale,
                                void* y, hipStream_t stream);
 

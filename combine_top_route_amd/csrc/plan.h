@@ -35,7 +35,12 @@ constexpr int kHdrPosReady = 224;      // layout workers whose positions are sto
 constexpr int kHdrCombineTicket = 256; // block ticket of the combine's later workgroups
 constexpr int kHdrDispatchTicket = 288; // block ticket of the dispatch's later workgroups
 constexpr int kHdrFusedBlockTicket = 320; // block ticket of the fused launch's later workgroups
+constexpr int kHdrSentTicket = 352;    // task ticket of the sentinel-readiness pipeline
+constexpr int kHdrSentDone = 384;      // workgroups finished in the sentinel-readiness pipeline
 constexpr size_t kHdrBytes = 2048;
+// Readiness sentinel of the sentinel-polling pipeline: every 32-bit word of a
+// receive row's first 16-byte unit while the row is empty (two bf16 NaNs).
+constexpr uint32_t kRowSentinelWord = 0xFFFFFFFFu;
 constexpr int kFlagStride = 32;        // uint32 per chunk ready flag (128 bytes)
 
 // Look-back state word (64 bits): the layout call's epoch in the high half;

@@ -73,8 +73,10 @@ typedef enum ubep_status {
     UBEP_ERR_TIMEOUT = 4,         /* device: a bounded wait on a ready flag expired */
     UBEP_ERR_HIP = 5,             /* a HIP runtime call failed                      */
     UBEP_ERR_BAD_POSITION = 6,    /* device: a pos entry outside [0, T*k)           */
-    UBEP_ERR_WORKSPACE = 7        /* device: workspace counters left inconsistent by
+    UBEP_ERR_WORKSPACE = 7,       /* device: workspace counters left inconsistent by
                                      a call that never finished; re-initialize it  */
+    UBEP_ERR_SENTINEL_DATA = 8    /* device: an x row's first 8 channels hold the
+                                     readiness sentinel word (bf16 NaN pair 0xFFFF) */
 } ubep_status;
 
 typedef enum ubep_dtype {
@@ -248,6 +250,38 @@ ubep_status ubep_dispatch_combine_chunked(const ubep_shape *shape /*host*/, cons
                                           void *out, const int32_t *chunk_order /*host*/,
                                           uint64_t spin_limit_ns, uint32_t debug_flags,
                                           void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Dispatch + combine in one persistent kernel with token-granular readiness
+ * carried by the data ("Data-as-Flag", its sentinel-polling variant: the
+ * consumer polls the payload itself for a value real data never takes,
+ * instead of a separate flag).  For identity experts and a bf16 payload
+ * (y = recv).  Per receive row: the producer writes channels 8.. of the row,
+ * waits until those stores have completed, then writes channels 0..7; the
+ * consumer polls channels 0..7 of each of its token's k rows until no 32-bit
+ * word there equals 0xFFFFFFFF (the sentinel: two bf16 NaNs), reads the rows,
+ * combines them, and writes the sentinel back.  Tasks are blocks of tokens
+ * handed out in token order from one counter (dispatch of block b + L, then
+ * combine of block b, for a lag L of about the resident workgroups).
+ * Preconditions: the first 16 bytes of every one of the T*k rows of recv
+ * hold the sentinel (ubep_recv_sentinel_init once after allocation; every
+ * call leaves them so again, also after a time-out); no aligned pair of
+ * channels among the first 8 of an x row is 0xFFFF 0xFFFF (reported as
+ * UBEP_ERR_SENTINEL_DATA, and that token's wait then times out).
+ * Results: out is bit-identical to ubep_dispatch(UBEP_BF16) + ubep_combine
+ * (y = recv); recv afterwards holds the dispatched rows except channels 0..7
+ * of every row, which hold the sentinel.  spin_limit_ns bounds the waits
+ * (0 selects one second); once one expires (UBEP_ERR_TIMEOUT) the rest give
+ * up at once.  debug_flags must be 0 in normal use; bit 0 withholds every
+ * row's channels 0..7 (only to exercise the time-out path). */
+ubep_status ubep_dispatch_combine_sentinel(const ubep_shape *shape /*host*/, const void *x,
+                                           const int32_t *pos, const float *topk_w, void *recv,
+                                           void *out, uint64_t spin_limit_ns, uint32_t debug_flags,
+                                           void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Write the readiness sentinel (0xFF bytes) into the first 16 bytes of each
+ * of `rows` receive rows of H bf16 channels (H % 8 == 0), as
+ * ubep_dispatch_combine_sentinel expects them before its first call. */
+ubep_status ubep_recv_sentinel_init(void *recv, int64_t rows, int64_t H, hipStream_t stream);
 
 /* Synchronise `stream`, read the device status word into *out (host) and
  * clear it.  Returns UBEP_OK if the read itself succeeded. */

@@ -135,3 +135,17 @@ def test_grouped_layout_validation_without_gpu():
     assert nws > 0
     assert L.ubep_layout_grouped(C.byref(big), 256, 256, 256, 256, 256, 256, 256, None, None, 256,
                                  nws, None) == ubep.ERR_UNSUPPORTED
+
+
+def test_sentinel_pipeline_validation_without_gpu():
+    L = ubep.lib()
+    s = ubep.ubep_shape(8, 64, 4, 2, 2, 1)
+    nws = L.ubep_workspace_bytes(C.byref(s))
+    assert L.ubep_dispatch_combine_sentinel(C.byref(s), 16, 16, 16, 16, None, 0, 0, 256, nws,
+                                            None) == ubep.ERR_INVALID_ARG          # no out
+    assert L.ubep_dispatch_combine_sentinel(C.byref(s), 16, 16, 16, 16, 16, 0, 2, 256, nws,
+                                            None) == ubep.ERR_INVALID_ARG          # unknown flag
+    assert L.ubep_recv_sentinel_init(256, 4, 12, None) == ubep.ERR_INVALID_ARG   # H % 8 != 0
+    assert L.ubep_recv_sentinel_init(8, 4, 16, None) == ubep.ERR_INVALID_ARG     # misaligned
+    assert L.ubep_recv_sentinel_init(256, 0, 16, None) == ubep.OK                # nothing to do
+    assert ubep.status_str(ubep.ERR_SENTINEL_DATA) == "input row holds the readiness sentinel word"
