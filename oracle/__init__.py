@@ -44,6 +44,10 @@ def lib():
         L.oracle_identity_fp8.restype = None
         L.oracle_combine.argtypes = [i64, i64, i32, p, p, p, p]
         L.oracle_combine.restype = None
+        L.oracle_expert_linear.argtypes = [i32, i64, i64, p, p, p, p]
+        L.oracle_expert_linear.restype = None
+        L.oracle_f64_to_bf16.argtypes = [C.c_double]
+        L.oracle_f64_to_bf16.restype = C.c_uint16
         L.oracle_gate.argtypes = [i64, i32, i32, i32, i32, C.c_int, p, p, p]
         L.oracle_gate.restype = C.c_int
         for n in ("oracle_f32_to_e4m3_array", "oracle_f32_to_bf16_array",
@@ -237,3 +241,20 @@ def pipeline_tokens(x, topk_idx, topk_w, E, R, C=1, payload="bf16", tokens=None)
         rows = (q.reshape(n, k, H), s.reshape(n, k, H // 128))
     out = combine(y, pos_local, ws)
     return rows, out
+
+
+def f64_to_bf16(v: float) -> int:
+    return int(lib().oracle_f64_to_bf16(float(v)))
+
+
+def expert_linear(x: np.ndarray, w: np.ndarray, expert_offset: np.ndarray) -> np.ndarray:
+    """y[r] = bf16(x[r] @ w[e].T) in double for the rows r of expert e's run.
+    x bf16 bits [rows, H]; w bf16 bits [E, N, H]; expert_offset int32 [E+1]."""
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    w = np.ascontiguousarray(w, dtype=np.uint16)
+    off = np.ascontiguousarray(expert_offset, dtype=np.int32)
+    E, N, H = w.shape
+    assert x.shape[1] == H and off.shape == (E + 1,) and off[-1] <= x.shape[0]
+    y = np.zeros((x.shape[0], N), np.uint16)
+    lib().oracle_expert_linear(E, H, N, _p(off), _p(x), _p(w), _p(y))
+    return y

@@ -448,3 +448,47 @@ int oracle_gate(int64_t T, int32_t E, int32_t k, int32_t groups, int32_t keep_gr
     free(allowed); free(taken); free(gscore); free(gtaken); free(val);
     return ORACLE_OK;
 }
+
+/* ------------------------------------------------------------------------ */
+/* per-expert linear map (a real expert between dispatch and combine)       */
+/* ------------------------------------------------------------------------ */
+
+/* Nearest bf16 (ties to even) of a finite double, rounded once from the
+ * double: 8 significant bits.  Results of magnitude below 2^-126 (bf16
+ * subnormals) are outside what this oracle is used for and go through fp32. */
+uint16_t oracle_f64_to_bf16(double v)
+{
+    if (v == 0.0) return signbit(v) ? 0x8000u : 0x0000u;
+    if (fabs(v) < 0x1p-126) return oracle_f32_to_bf16((float)v);
+    int ex;
+    double m = frexp(v, &ex);            /* v = m * 2^ex, 0.5 <= |m| < 1 */
+    double q = nearbyint(m * 256.0);     /* 8 significant bits, ties to even */
+    float f = (float)ldexp(q, ex - 8);   /* exact: 8 bits fit in fp32 */
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    return (uint16_t)(u >> 16);
+}
+
+/* y[r][n] = bf16( sum over c of x[r][c] * w[e][n][c] ) for every row r of
+ * expert e's run [expert_offset[e], expert_offset[e+1]), the sum taken
+ * in double (exact for H <= 2^22 products of bf16 values, up to the final
+ * rounding of the sum itself) and rounded once to bf16.  x and y are bf16
+ * [rows][H] and [rows][N]; w is bf16 [E][N][H] (row n of expert e's weight,
+ * channels contiguous). */
+void oracle_expert_linear(int32_t E, int64_t H, int64_t N, const int32_t *expert_offset,
+                          const uint16_t *x, const uint16_t *w, uint16_t *y)
+{
+    for (int32_t e = 0; e < E; ++e) {
+        const uint16_t *we = w + (int64_t)e * N * H;
+        for (int64_t r = expert_offset[e]; r < expert_offset[e + 1]; ++r) {
+            const uint16_t *xr = x + r * H;
+            for (int64_t n = 0; n < N; ++n) {
+                const uint16_t *wn = we + n * H;
+                double acc = 0.0;
+                for (int64_t c = 0; c < H; ++c)
+                    acc += (double)oracle_bf16_to_f32(xr[c]) * (double)oracle_bf16_to_f32(wn[c]);
+                y[r * N + n] = oracle_f64_to_bf16(acc);
+            }
+        }
+    }
+}

@@ -33,4 +33,8 @@ enum { ORACLE_GATE_SOFTMAX = 0, ORACLE_GATE_SIGMOID = 1 };
 int oracle_gate(int64_t T, int32_t E, int32_t k, int32_t groups, int32_t keep_groups, int norm,
                 const float *logits, int32_t *topk_idx, float *topk_w);
 
+uint16_t oracle_f64_to_bf16(double v);
+void oracle_expert_linear(int32_t E, int64_t H, int64_t N, const int32_t *expert_offset,
+                          const uint16_t *x, const uint16_t *w, uint16_t *y);
+
 #endif
