@@ -40,17 +40,21 @@ HBM_PEAK_GBS = 8000.0
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "hbm_counters.txt")
 
 
-def algorithmic_bytes(s: dict, fp8: bool, gate: bool = False) -> dict:
+def algorithmic_bytes(s: dict, fp8: bool, gate: bool = False, expert_w_bytes: int = -1) -> dict:
+    """expert_w_bytes >= 0: the step also runs the per-expert linear map (N = H),
+    which reads the weights of the experts that received rows (that many
+    bytes), the T*k receive rows, and writes T*k output rows."""
     T, H, k = s["T"], s["H"], s["k"]
     layout = 8 * T * k
     gate_b = 4 * T * s["E"] + 8 * T * k if gate else 0
+    expert = expert_w_bytes + 4 * T * k * H + 4 * (s["E"] + 1) if expert_w_bytes >= 0 else 0
     if fp8:
         dispatch = 2 * T * H + 4 * T * k + T * k * H + 4 * T * k * (H // 128)
     else:
         dispatch = 2 * T * H + 4 * T * k + 2 * T * k * H
     combine = 2 * T * k * H + 8 * T * k + 2 * T * H
-    return dict(gate=gate_b, layout=layout, dispatch=dispatch, combine=combine,
-                total=gate_b + layout + dispatch + combine)
+    return dict(gate=gate_b, layout=layout, dispatch=dispatch, combine=combine, expert=expert,
+                total=gate_b + layout + dispatch + expert + combine)
 
 
 def source_hash() -> str:
@@ -194,12 +198,14 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=None, help="workload name (default: DeepSeek-V3 decode)")
-    ap.add_argument("--mode", choices=["unfused", "chunked", "sentinel", "gated", "fused"],
+    ap.add_argument("--mode", choices=["unfused", "chunked", "sentinel", "gated", "fused", "moe"],
                     default="unfused",
                     help="gated: the step starts from router logits (ubep_gate, then unfused); "
                          "fused: ubep_layout_dispatch (one launch), then combine; "
                          "sentinel: layout, then ubep_dispatch_combine_sentinel (token-granular "
-                         "readiness polled in the rows)")
+                         "readiness polled in the rows); moe: expert-grouped layout, dispatch, "
+                         "a per-expert H x H linear map on the matrix cores (random bf16 "
+                         "weights), combine")
     ap.add_argument("--order", choices=["rank", "expert"], default="rank",
                     help="receive order inside a rank's region: (token, slot) with ubep_layout, or "
                          "expert-grouped (expert, token, slot) with ubep_layout_grouped")
@@ -236,7 +242,9 @@ def main(argv=None):
     sd = s.as_dict()
     fp8 = w.recipe.payload == "fp8"
     dtype = ubep.FP8_E4M3 if fp8 else ubep.BF16
-    if args.mode in ("chunked", "sentinel") and fp8:
+    if args.mode == "moe":
+        args.order = "expert"
+    if args.mode in ("chunked", "sentinel", "moe") and fp8:
         print("the pipelined kernels carry a bf16 payload only", file=sys.stderr)
         return 2
     if args.mode == "fused" and args.order == "expert":
@@ -257,6 +265,13 @@ def main(argv=None):
                           else ["dispatch", "combine"])
     if args.mode == "sentinel":
         ubep.ubep_recv_sentinel_init(b.recv, s.T * s.k, s.H)
+    moe = args.mode == "moe"
+    if moe:
+        calls = ["layout", "dispatch", "expert", "combine"]
+        gen = torch.Generator(device="cuda").manual_seed(w.recipe.seed)
+        wexp = torch.randn((s.E, s.H, s.H), generator=gen, dtype=torch.bfloat16, device="cuda")
+        wexp.mul_(1.0 / float(s.H) ** 0.5)
+        yexp = torch.empty((s.T * s.k, s.H), dtype=torch.bfloat16, device="cuda")
     if args.mode == "fused":
         if fp8:
             print("the fused launch carries a bf16 payload only", file=sys.stderr)
@@ -286,6 +301,8 @@ def main(argv=None):
             ubep.ubep_layout_dispatch(sd, b.topk_idx, b.x, b.pos, b.expert_count, b.rank_count,
                                       b.recv_offset, b.send_offset, chunk_off, None, b.recv, b.ws,
                                       stream)
+        elif name == "expert":
+            ubep.ubep_expert_linear(sd, s.H, expert_off, b.recv, wexp, yexp, b.ws, stream)
         elif name == "sentinel":
             ubep.ubep_dispatch_combine_sentinel(sd, b.x, b.pos, b.topk_w, b.recv, b.out, b.ws,
                                                 stream=stream)
@@ -295,7 +312,7 @@ def main(argv=None):
         elif name == "dispatch":
             ubep.ubep_dispatch(sd, dtype, b.x, b.pos, b.recv, b.recv_scale, b.ws, stream)
         else:
-            ubep.ubep_combine(sd, b.y, b.pos, b.topk_w, b.out, b.ws, stream)
+            ubep.ubep_combine(sd, yexp if moe else b.y, b.pos, b.topk_w, b.out, b.ws, stream)
 
     hev = HipEvents()
 
@@ -325,6 +342,10 @@ def main(argv=None):
     if st != ubep.OK:
         print(f"device status after warm-up: {ubep.STATUS_NAMES.get(st, st)}", file=sys.stderr)
         return 1
+
+    ew_bytes = -1
+    if moe:    # weights of the experts that received rows are what the expert must read
+        ew_bytes = int((b.expert_count > 0).sum().item()) * s.H * s.H * 2
 
     # untimed calibration: every kernel timed by its own launch, to find the
     # dominant one
@@ -430,7 +451,7 @@ def main(argv=None):
         (gw, _), (gc, gc_steps) = graph_pass(False), graph_pass(True)
         passes = {"warm": (gw, eager["warm"][1], eager["warm"][2], None),
                   "cold": (gc, eager["cold"][1], eager["cold"][2], gc_steps)}
-    ceiling = copy_ceiling(algorithmic_bytes(sd, fp8, gated)["total"])
+    ceiling = copy_ceiling(algorithmic_bytes(sd, fp8, gated, ew_bytes)["total"])
     hev.close()
     st = ubep.ubep_get_device_status(b.ws)
     if st != ubep.OK:
@@ -443,7 +464,7 @@ def main(argv=None):
     def pct(q):
         return round(cold_steps[min(len(cold_steps) - 1, int(q * len(cold_steps)))] / 1e3, 5)
 
-    nb = algorithmic_bytes(sd, fp8, gated)
+    nb = algorithmic_bytes(sd, fp8, gated, ew_bytes)
     gbs = nb["total"] / (ms * 1e-3) / 1e9
     dom_bytes = nb["dispatch"] + nb["combine"] if dom in ("chunked", "sentinel") else nb[dom]
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
@@ -492,6 +513,11 @@ def main(argv=None):
                 "caches": ("cold: 512 MB read between steps" if other == "cold"
                            else "warm: back-to-back steps")},
         "rank_skew_max_over_mean": round(float(rc.max() / rc.mean()), 3),
+        "expert": ({"flops": 2 * s.T * s.k * s.H * s.H,
+                    "ms_calibration": round(per_call["expert"] / 1e3, 5),
+                    "tflops": round(2 * s.T * s.k * s.H * s.H / (per_call["expert"] * 1e-6) / 1e12, 1),
+                    "mfma_bf16_peak_tflops": 2500.0,
+                    "weight_bytes": ew_bytes} if moe else None),
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),

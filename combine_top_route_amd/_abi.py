@@ -79,6 +79,7 @@ def lib() -> C.CDLL:
             "ubep_dispatch_combine_chunked": ([S, P, P, P, P, P, P, U64, U32, P, SZ, P], C.c_int),
             "ubep_dispatch_combine_sentinel": ([S, P, P, P, P, P, U64, U32, P, SZ, P], C.c_int),
             "ubep_recv_sentinel_init": ([P, I64, I64, P], C.c_int),
+            "ubep_expert_linear": ([S, I64, P, P, P, P, P, SZ, P], C.c_int),
             "ubep_get_device_status": ([P, SZ, P, C.POINTER(C.c_int)], C.c_int),
             "ubep_identity_expert_fp8": ([I64, I64, P, P, P, P], C.c_int),
             "ubep_copy": ([P, P, SZ, P], C.c_int),
@@ -219,6 +220,13 @@ def ubep_dispatch_combine_sentinel(shape, x, pos, topk_w, recv, out, ws, spin_li
 def ubep_recv_sentinel_init(recv, rows, H, stream=None):
     _check(lib().ubep_recv_sentinel_init(_ptr(recv), rows, H, _stream(stream)),
            "ubep_recv_sentinel_init")
+
+
+def ubep_expert_linear(shape, N, expert_offset, x, w, y, ws, stream=None):
+    s = _shape(shape)
+    _check(lib().ubep_expert_linear(C.byref(s), int(N), _ptr(expert_offset), _ptr(x), _ptr(w),
+                                    _ptr(y), _ptr(ws), _nbytes(ws), _stream(stream)),
+           "ubep_expert_linear")
 
 
 def ubep_get_device_status(ws, stream=None) -> int:

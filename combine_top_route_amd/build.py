@@ -17,7 +17,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libubep.so")
 SOURCES = ["api.hip", "gate.hip", "layout.hip", "layout_dispatch.hip", "dispatch.hip", "combine.hip",
-           "chunked.hip", "sentinel.hip", "aux.hip"]
+           "chunked.hip", "sentinel.hip", "expert.hip", "aux.hip"]
 ARCH = os.environ.get("UBEP_OFFLOAD_ARCH", "gfx950")
 
 # -amdgpu-atomic-optimizer-strategy=None: every device atomic here is issued by

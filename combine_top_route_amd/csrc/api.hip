@@ -317,6 +317,24 @@ ubep_status ubep_recv_sentinel_init(void* recv, int64_t rows, int64_t H, hipStre
     return hip_status(launch_sentinel_fill(recv, rows, H, stream));
 }
 
+ubep_status ubep_expert_linear(const ubep_shape* s, int64_t N, const int32_t* expert_offset,
+                               const void* x, const void* w, void* y, void* ws, size_t ws_bytes,
+                               hipStream_t stream) {
+    const ubep_status st = ubep_check_shape(s, UBEP_BF16);
+    if (st != UBEP_OK) return st;
+    if (!expert_offset || !x || !w || !y || !ws || ws_bytes < kHdrBytes) return UBEP_ERR_INVALID_ARG;
+    if (N <= 0 || N % 128 != 0 || s->H % 64 != 0) return UBEP_ERR_UNSUPPORTED;
+    if (!aligned(x, 16) || !aligned(w, 16) || !aligned(y, 16) || !aligned(ws, 256) ||
+        !aligned(expert_offset, 4))
+        return UBEP_ERR_INVALID_ARG;
+    const int64_t rows = s->T * (int64_t)s->k;
+    if (s->E > kExpertMaxE || (rows + 127) / 128 + s->E > kExpertMaxRowTiles || N / 128 > (1 << 30) ||
+        N >= ((int64_t)1 << 30))
+        return UBEP_ERR_UNSUPPORTED;
+    uint32_t* status = static_cast<uint32_t*>(ws) + kHdrStatus;
+    return hip_status(launch_expert_linear(s->E, s->H, N, rows, expert_offset, x, w, y, status, stream));
+}
+
 ubep_status ubep_get_device_status(void* ws, size_t ws_bytes, hipStream_t stream,
                                    ubep_status* out) {
     if (ws == nullptr || out == nullptr || ws_bytes < kHdrBytes || !aligned(ws, 256))

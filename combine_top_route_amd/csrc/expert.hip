@@ -1,0 +1,198 @@
+// Per-expert linear map on the expert-grouped receive rows: the real expert
+// computation that sits between dispatch and combine (the opening section of
+// "NJU x Huawei UBEP: Reengineering MoE Expert Parallelism": each token is
+// processed by the experts it selected and the results are gathered back).
+//
+//   y[r][n] = bf16( sum over c of x[r][c] * w[e][n][c] )   for r in expert e's run
+//
+// A dense contraction per expert, so it runs on the matrix cores:
+// v_mfma_f32_16x16x32_bf16 (gfx950) with fp32 accumulation.  A workgroup of
+// 4 waves computes a 128 (output channels) x 128 (rows) tile of one expert;
+// each wave a 64 x 64 quarter as 4 x 4 MFMA tiles.  The weight rows are the
+// MFMA's A operand and the receive rows its B operand, both read as 16-byte
+// runs of 8 channels, so each lane's 4 accumulator values are 4 consecutive
+// output channels of one row (one 8-byte store).  k steps of 64 channels are
+// staged through LDS (rows padded by 16 bytes), and the next step's global
+// loads are in flight while the current step's MFMAs run.
+//
+// Tiles: blockIdx.x is the output-channel tile, blockIdx.y a row tile counted
+// over all experts in expert order (expert e owns ceil(count_e / 128) of
+// them); each workgroup finds its expert from expert_offset with one
+// workgroup-wide scan, so no host round trip is needed between the layout
+// and this kernel.  Rows past the run's end are loaded as zeros and not
+// stored.  Consecutive workgroups share a row tile and walk the output
+// channels, so the tile's receive rows stay in L2 while the weights stream.
+#include "launch.h"
+#include "rows.h"
+
+namespace ubep {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kGemmThreads = 256;
+constexpr int kBN = 128;                 // output channels per tile
+constexpr int kBM = 128;                 // rows per tile
+constexpr int kBK = 64;                  // channels per k step
+constexpr int kLdsStride = kBK + 8;      // bf16 per LDS row: 144 bytes
+constexpr int kPerThreadE = kExpertMaxE / kGemmThreads;
+constexpr int kVecPerRow = kBK / 8;                          // 16-byte vectors per tile row
+constexpr int kLoadsPerThread = kBM * kVecPerRow / kGemmThreads;
+static_assert(kBM == kBN, "one load mapping serves both tiles");
+
+struct ExpertArgs {
+    const int32_t* eoff;     // [E+1]
+    const u32x4* x;          // [n_rows][H/8]
+    const u32x4* w;          // [E][N][H/8]
+    uint2* y;                // [n_rows][N/4]
+    uint32_t* status;
+    int64_t H, N, n_rows;
+    int32_t E;
+};
+
+__device__ __forceinline__ uint2 pack_bf16x4(f32x4 v) {
+    uint2 o;
+    o.x = f32_to_bf16(v[0]) | (f32_to_bf16(v[1]) << 16);
+    o.y = f32_to_bf16(v[2]) | (f32_to_bf16(v[3]) << 16);
+    return o;
+}
+
+__global__ __launch_bounds__(kGemmThreads) void expert_linear_kernel(ExpertArgs a) {
+    __shared__ __attribute__((aligned(16))) uint16_t s_w[kBN * kLdsStride];
+    __shared__ __attribute__((aligned(16))) uint16_t s_x[kBM * kLdsStride];
+    __shared__ int32_t s_wsum[kGemmThreads / 64];
+    __shared__ int32_t s_sel[2];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int32_t m = (int32_t)blockIdx.y;
+    const int64_t n0 = (int64_t)blockIdx.x * kBN;
+
+    // ---- which expert and which of its row tiles this workgroup takes
+    int32_t cnt[kPerThreadE];
+    int32_t mine = 0;
+#pragma unroll
+    for (int i = 0; i < kPerThreadE; ++i) {
+        const int32_t e = tid * kPerThreadE + i;
+        int32_t c = 0;
+        if (e < a.E) {
+            const int32_t rows = a.eoff[e + 1] - a.eoff[e];
+            c = rows > 0 ? (rows + kBM - 1) / kBM : 0;
+        }
+        cnt[i] = c;
+        mine += c;
+    }
+    int32_t inc = mine;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int32_t u = __shfl_up(inc, o, 64);
+        if (lane >= o) inc += u;
+    }
+    if (lane == 63) s_wsum[wave] = inc;
+    if (tid == 0) s_sel[0] = -1;
+    __syncthreads();
+    int32_t run = inc - mine;
+    for (int i = 0; i < wave; ++i) run += s_wsum[i];
+#pragma unroll
+    for (int i = 0; i < kPerThreadE; ++i) {
+        if (cnt[i] > 0 && m >= run && m < run + cnt[i]) {
+            s_sel[0] = tid * kPerThreadE + i;
+            s_sel[1] = m - run;
+        }
+        run += cnt[i];
+    }
+    __syncthreads();
+    const int32_t e = s_sel[0];
+    if (e < 0) return;                                   // past the last tile (uniform)
+    const int64_t run_lo = a.eoff[e], r_end = a.eoff[e + 1];
+    if (run_lo < 0 || r_end > a.n_rows) {                // inconsistent offsets
+        if (tid == 0) raise_status(a.status, UBEP_ERR_BAD_POSITION);
+        return;
+    }
+    const int64_t r_lo = run_lo + (int64_t)s_sel[1] * kBM;
+
+    // ---- k loop
+    const int64_t nvh = a.H / 8;
+    const u32x4* wt = a.w + ((int64_t)e * a.N + n0) * nvh;
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+    u32x4 pw[kLoadsPerThread], px[kLoadsPerThread];
+    auto load_step = [&](int64_t kv) {                   // kv: 16-byte vector offset of the step
+#pragma unroll
+        for (int i = 0; i < kLoadsPerThread; ++i) {
+            const int q = tid + kGemmThreads * i;        // 128 rows x kVecPerRow vectors
+            const int row = q / kVecPerRow, cv = q % kVecPerRow;
+            pw[i] = wt[(int64_t)row * nvh + kv + cv];
+            const int64_t r = r_lo + row;
+            px[i] = r < r_end ? a.x[r * nvh + kv + cv] : zero;
+        }
+    };
+    f32x4 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+    const int wn = (wave & 1) * 64, wm = (wave >> 1) * 64;
+    const int fr = lane & 15, fk = (lane >> 4) * 8;      // fragment row and channel offset
+    const int64_t nk = a.H / kBK;
+    load_step(0);
+    for (int64_t kt = 0; kt < nk; ++kt) {
+        __syncthreads();                                 // the last step's fragments are read
+#pragma unroll
+        for (int i = 0; i < kLoadsPerThread; ++i) {
+            const int q = tid + kGemmThreads * i;
+            const int row = q / kVecPerRow, cv = q % kVecPerRow;
+            *reinterpret_cast<u32x4*>(&s_w[row * kLdsStride + cv * 8]) = pw[i];
+            *reinterpret_cast<u32x4*>(&s_x[row * kLdsStride + cv * 8]) = px[i];
+        }
+        __syncthreads();
+        if (kt + 1 < nk) load_step((kt + 1) * (kBK / 8)); // next step's loads overlap the MFMAs
+#pragma unroll
+        for (int ks = 0; ks < kBK; ks += 32) {
+            bf16x8 fa[4], fb[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                fa[i] = *reinterpret_cast<const bf16x8*>(&s_w[(wn + 16 * i + fr) * kLdsStride + ks + fk]);
+                fb[i] = *reinterpret_cast<const bf16x8*>(&s_x[(wm + 16 * i + fr) * kLdsStride + ks + fk]);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+        }
+    }
+
+    // ---- epilogue: lane holds channels n .. n+3 of row r for each (i, j)
+    const int64_t nq = a.N / 4;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int64_t r = r_lo + wm + 16 * j + fr;
+        if (r >= r_end) continue;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int64_t n = n0 + wn + 16 * i + (lane >> 4) * 4;
+            a.y[r * nq + n / 4] = pack_bf16x4(acc[i][j]);
+        }
+    }
+}
+
+hipError_t launch_expert_linear(int32_t E, int64_t H, int64_t N, int64_t n_rows,
+                                const int32_t* expert_offset, const void* x, const void* w, void* y,
+                                uint32_t* status, hipStream_t stream) {
+    ExpertArgs a;
+    a.eoff = expert_offset;
+    a.x = static_cast<const u32x4*>(x);
+    a.w = static_cast<const u32x4*>(w);
+    a.y = static_cast<uint2*>(y);
+    a.status = status;
+    a.H = H;
+    a.N = N;
+    a.n_rows = n_rows;
+    a.E = E;
+    // row tiles over all experts: at most ceil(n_rows / 128) + E (one partial tile each)
+    const int64_t row_tiles = (n_rows + kBM - 1) / kBM + E;
+    return launch_kernel(expert_linear_kernel, dim3((unsigned)(N / kBN), (unsigned)row_tiles),
+                         dim3(kGemmThreads), 0, stream, a);
+}
+
+}  // namespace ubep

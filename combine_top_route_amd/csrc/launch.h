@@ -76,6 +76,10 @@ hipError_t launch_sentinel_pipeline(const Plan& p, const void* x, const int32_t*
                                     uint32_t debug_flags, void* ws, int device, hipStream_t stream);
 hipError_t launch_sentinel_fill(void* recv, int64_t rows, int64_t H, hipStream_t stream);
 
+hipError_t launch_expert_linear(int32_t E, int64_t H, int64_t N, int64_t n_rows,
+                                const int32_t* expert_offset, const void* x, const void* w, void* y,
+                                uint32_t* status, hipStream_t stream);
+
 hipError_t launch_identity_fp8(int64_t rows, int64_t H, const uint8_t* q, const float* scale,
                                void* y, hipStream_t stream);
 

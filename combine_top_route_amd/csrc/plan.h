@@ -15,6 +15,8 @@ constexpr int kMaxE = 8192;
 constexpr int kMaxC = 256;
 constexpr int kGateMaxE = 1024;
 constexpr int kGateMaxGroups = 64;
+constexpr int kExpertMaxE = 1024;        // experts of ubep_expert_linear
+constexpr int64_t kExpertMaxRowTiles = 65535;   // row tiles (grid.y) of ubep_expert_linear
 
 // Layout kernel: 8 waves per workgroup, tiles of whole tokens with at most
 // kTileRowsMax rows.

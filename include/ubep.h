@@ -283,6 +283,26 @@ ubep_status ubep_dispatch_combine_sentinel(const ubep_shape *shape /*host*/, con
  * ubep_dispatch_combine_sentinel expects them before its first call. */
 ubep_status ubep_recv_sentinel_init(void *recv, int64_t rows, int64_t H, hipStream_t stream);
 
+/* Per-expert linear map on expert-grouped receive rows: the expert itself,
+ * between dispatch and combine (opening section of the UBEP page: each token
+ * is processed by the experts it selected, then gathered back).  For every
+ * expert e and every row r in [expert_offset[e], expert_offset[e+1]):
+ *   y[r][n] = bf16( sum over c of x[r][c] * w[e][n][c] ),  n = 0..N-1,
+ * with bf16 products accumulated in fp32 on the matrix cores (the order of
+ * the accumulation is the hardware's) and one round to nearest even.
+ * x: bf16 [T*k][H], rows in the order of ubep_layout_grouped (its pos and
+ * expert_offset); w: bf16 [E][N][H] (row n of expert e's weight, channels
+ * contiguous); y: bf16 [T*k][N] (with N = H it is combine's input).
+ * expert_offset: int32 [E+1] device array, non-decreasing from 0 to at most
+ * T*k (ubep_layout_grouped's output); rows outside every run are not written.
+ * Limits: H % 64 == 0, N % 128 == 0, E <= 1024, ceil(T*k/128) + E <= 65535
+ * (else UBEP_ERR_UNSUPPORTED).  An offset outside [0, T*k] sets
+ * UBEP_ERR_BAD_POSITION and that expert's rows are skipped.  The workspace
+ * is used for the status word only.  One kernel on `stream`. */
+ubep_status ubep_expert_linear(const ubep_shape *shape /*host*/, int64_t N,
+                               const int32_t *expert_offset, const void *x, const void *w,
+                               void *y, void *ws, size_t ws_bytes, hipStream_t stream);
+
 /* Synchronise `stream`, read the device status word into *out (host) and
  * clear it.  Returns UBEP_OK if the read itself succeeded. */
 ubep_status ubep_get_device_status(void *ws, size_t ws_bytes, hipStream_t stream,

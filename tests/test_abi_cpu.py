@@ -149,3 +149,18 @@ def test_sentinel_pipeline_validation_without_gpu():
     assert L.ubep_recv_sentinel_init(8, 4, 16, None) == ubep.ERR_INVALID_ARG     # misaligned
     assert L.ubep_recv_sentinel_init(256, 0, 16, None) == ubep.OK                # nothing to do
     assert ubep.status_str(ubep.ERR_SENTINEL_DATA) == "input row holds the readiness sentinel word"
+
+
+def test_expert_linear_validation_without_gpu():
+    L = ubep.lib()
+    s = ubep.ubep_shape(64, 128, 8, 2, 2, 1)
+    assert L.ubep_expert_linear(C.byref(s), 100, 256, 256, 256, 256, 256, 4096,
+                                None) == ubep.ERR_UNSUPPORTED           # N % 128 != 0
+    s2 = ubep.ubep_shape(64, 96, 8, 2, 2, 1)
+    assert L.ubep_expert_linear(C.byref(s2), 128, 256, 256, 256, 256, 256, 4096,
+                                None) == ubep.ERR_UNSUPPORTED           # H % 64 != 0
+    assert L.ubep_expert_linear(C.byref(s), 128, None, 256, 256, 256, 256, 4096,
+                                None) == ubep.ERR_INVALID_ARG           # no expert_offset
+    big = ubep.ubep_shape(2048, 128, 2048, 2, 2, 1)
+    assert L.ubep_expert_linear(C.byref(big), 128, 256, 256, 256, 256, 256, 4096,
+                                None) == ubep.ERR_UNSUPPORTED           # E > 1024
