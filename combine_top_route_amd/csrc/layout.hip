@@ -27,7 +27,7 @@ template <int LR, bool EORD>
 __global__ __launch_bounds__(kLayoutThreads) void layout_kernel(LayoutArgs a) {
     extern __shared__ int32_t dyn_lds[];
     const uint32_t epoch = ld_relaxed(&a.hdr[kHdrLayoutEpoch]);
-    const LayoutLds L = carve_lds(dyn_lds, a.p, kLayoutWaves);
+    const LayoutLds L = carve_lds<EORD>(dyn_lds, a.p, kLayoutWaves);
     uint32_t done = 0;
     layout_worker<kLayoutWaves, LR, false, kLookbackWindow, EORD>(a, L, epoch, blockIdx.x, gridDim.x,
                                                                  &done);

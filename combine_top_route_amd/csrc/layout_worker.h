@@ -55,13 +55,13 @@ struct LayoutArgs {
     int32_t* send_offset;
     int32_t* chunk_offset;   // may be null
     int32_t* recv_src;       // may be null
-    int32_t* expert_offset;  // [E+1], expert order only (may be null)
     uint32_t* hdr;
     uint64_t* state;         // [n_tiles][R + E]
     int32_t* excl;           // [n_tiles][K]
     int32_t* wbase;          // [n_tiles][NW][K]
     Plan p;
     uint64_t spin_ticks;
+    int32_t* expert_offset;  // [E+1], expert order only (may be null)
 };
 
 // LDS of one worker, carved from the kernel's dynamic shared memory.
@@ -87,14 +87,16 @@ inline int64_t layout_lds_bytes(const Plan& p, int nw) {
     return 4 * ((int64_t)nw * p.K + p.E + 3 * (int64_t)p.K + kMaxTilesPerGroup + nw + 1 + bins);
 }
 
+template <bool EORD = false>
 __device__ __forceinline__ LayoutLds carve_lds(int32_t* base, const Plan& p, int nw) {
+    const int32_t K = EORD ? p.K : p.R;
     LayoutLds L;
     L.wh = base;
-    L.eh = L.wh + nw * p.K;
+    L.eh = L.wh + nw * K;
     L.cnt = L.eh + p.E;
-    L.excl = L.cnt + p.K;
-    L.off = L.excl + p.K;
-    L.tiles = reinterpret_cast<uint32_t*>(L.off + p.K);
+    L.excl = L.cnt + K;
+    L.off = L.excl + K;
+    L.tiles = reinterpret_cast<uint32_t*>(L.off + K);
     L.tmp = reinterpret_cast<int32_t*>(L.tiles + kMaxTilesPerGroup);
     L.ticket = reinterpret_cast<uint32_t*>(L.tmp + nw);
     L.bins = reinterpret_cast<int32_t*>(L.ticket + 1);

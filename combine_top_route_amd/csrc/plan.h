@@ -76,15 +76,6 @@ struct Plan {
     int32_t dbits;         // bits to hold a rank id (0..R-1)
     int32_t ebits;         // bits to hold an expert id (0..E-1)
     int32_t gather;        // 1: prefixes and totals by gathering all tiles' counts
-    // Position keys.  Rank order: rows sort by (rank, token, slot), one key per
-    // rank.  Expert order: rows sort by (expert, token, slot), one key per
-    // expert (a rank's experts are consecutive, so its region is still one
-    // run).  key(e) = rank_of(e, key_magic).
-    int32_t order;         // 0: rank order, 1: expert order
-    int32_t K;             // keys: R or E
-    uint32_t key_magic;    // epr_magic (rank order) or 0 (expert order: key = e)
-    int32_t kbits;         // bits to hold a key
-    int32_t kcol;          // state digit of key 0: 0 (rank digits) or R (expert digits)
     // workspace byte offsets
     int32_t slots;         // look-back digits per tile: R ranks, then E experts
     size_t off_state;      // uint64 [n_tiles][R+E]  look-back state
@@ -92,6 +83,16 @@ struct Plan {
     size_t off_wbase;      // int32  [n_tiles][8][K] rows with key q in earlier waves of the tile
     size_t off_flags;      // uint32 [C][kFlagStride] chunk ready flags
     size_t ws_bytes;
+    // Position keys (last, so that the fields the rank-order kernels read keep
+    // their places).  Rank order: rows sort by (rank, token, slot), one key
+    // per rank.  Expert order: rows sort by (expert, token, slot), one key per
+    // expert (a rank's experts are consecutive, so its region is still one
+    // run).  key(e) = rank_of(e, key_magic).
+    int32_t order;         // 0: rank order, 1: expert order
+    int32_t K;             // keys: R or E
+    uint32_t key_magic;    // epr_magic (rank order) or 0 (expert order: key = e)
+    int32_t kbits;         // bits to hold a key
+    int32_t kcol;          // state digit of key 0: 0 (rank digits) or R (expert digits)
 };
 
 // Host: fill `p` for a shape that passed validation; order 0 (rank order)
