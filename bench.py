@@ -57,10 +57,19 @@ def algorithmic_bytes(s: dict, fp8: bool, gate: bool = False, expert_w_bytes: in
                 total=gate_b + layout + dispatch + expert + combine)
 
 
-def source_hash() -> str:
+# the sources each counted kernel is built from (its own file and the headers
+# it includes); counters taken on other sources are not used
+KERNEL_SOURCES = {
+    "combine": ["combine.hip", "rows.h", "launch.h", "device_common.h", "plan.h"],
+    "dispatch": ["dispatch.hip", "rows.h", "launch.h", "device_common.h", "plan.h"],
+    "layout": ["layout.hip", "layout_worker.h", "launch.h", "device_common.h", "plan.h"],
+}
+
+
+def source_hash(kernel: str) -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "combine_top_route_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
+    for f in sorted(KERNEL_SOURCES.get(kernel, os.listdir(csrc))):
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + b"\0" + fh.read())
     return h.hexdigest()[:16]
@@ -82,7 +91,7 @@ def read_counters(kernel: str, workload: str):
             rows[(kv.get("kind"), kv.get("kernel"), kv.get("workload"))] = kv
     cal = next((v for (kind, _, _), v in rows.items() if kind == "copy"), None)
     got = rows.get(("kernel", kernel, workload))
-    if cal is None or got is None or got.get("source") != source_hash():
+    if cal is None or got is None or got.get("source") != source_hash(kernel):
         return None
     copy_bytes = float(cal["bytes"])
     f_scale = copy_bytes / (float(cal["fetch_kib"]) * 1024.0)
