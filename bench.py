@@ -280,6 +280,9 @@ def main(argv=None):
         gen = torch.Generator(device="cuda").manual_seed(w.recipe.seed)
         wexp = torch.randn((s.E, s.H, s.H), generator=gen, dtype=torch.bfloat16, device="cuda")
         wexp.mul_(1.0 / float(s.H) ** 0.5)
+        wpacked = torch.empty_like(wexp)
+        ubep.ubep_expert_pack_weights(s.E, s.H, s.H, wexp, wpacked)
+        del wexp
         yexp = torch.empty((s.T * s.k, s.H), dtype=torch.bfloat16, device="cuda")
     if args.mode == "fused":
         if fp8:
@@ -311,7 +314,7 @@ def main(argv=None):
                                       b.recv_offset, b.send_offset, chunk_off, None, b.recv, b.ws,
                                       stream)
         elif name == "expert":
-            ubep.ubep_expert_linear(sd, s.H, expert_off, b.recv, wexp, yexp, b.ws, stream)
+            ubep.ubep_expert_linear(sd, s.H, expert_off, b.recv, wpacked, yexp, b.ws, stream)
         elif name == "sentinel":
             ubep.ubep_dispatch_combine_sentinel(sd, b.x, b.pos, b.topk_w, b.recv, b.out, b.ws,
                                                 stream=stream)

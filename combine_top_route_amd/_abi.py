@@ -80,6 +80,7 @@ def lib() -> C.CDLL:
             "ubep_dispatch_combine_sentinel": ([S, P, P, P, P, P, U64, U32, P, SZ, P], C.c_int),
             "ubep_recv_sentinel_init": ([P, I64, I64, P], C.c_int),
             "ubep_expert_linear": ([S, I64, P, P, P, P, P, SZ, P], C.c_int),
+            "ubep_expert_pack_weights": ([I32, I64, I64, P, P, P], C.c_int),
             "ubep_get_device_status": ([P, SZ, P, C.POINTER(C.c_int)], C.c_int),
             "ubep_identity_expert_fp8": ([I64, I64, P, P, P, P], C.c_int),
             "ubep_copy": ([P, P, SZ, P], C.c_int),
@@ -227,6 +228,11 @@ def ubep_expert_linear(shape, N, expert_offset, x, w, y, ws, stream=None):
     _check(lib().ubep_expert_linear(C.byref(s), int(N), _ptr(expert_offset), _ptr(x), _ptr(w),
                                     _ptr(y), _ptr(ws), _nbytes(ws), _stream(stream)),
            "ubep_expert_linear")
+
+
+def ubep_expert_pack_weights(E, N, H, w, packed, stream=None):
+    _check(lib().ubep_expert_pack_weights(int(E), int(N), int(H), _ptr(w), _ptr(packed),
+                                          _stream(stream)), "ubep_expert_pack_weights")
 
 
 def ubep_get_device_status(ws, stream=None) -> int:

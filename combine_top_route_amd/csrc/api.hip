@@ -323,7 +323,7 @@ ubep_status ubep_expert_linear(const ubep_shape* s, int64_t N, const int32_t* ex
     const ubep_status st = ubep_check_shape(s, UBEP_BF16);
     if (st != UBEP_OK) return st;
     if (!expert_offset || !x || !w || !y || !ws || ws_bytes < kHdrBytes) return UBEP_ERR_INVALID_ARG;
-    if (N <= 0 || N % 128 != 0 || s->H % 64 != 0) return UBEP_ERR_UNSUPPORTED;
+    if (N <= 0 || N % 128 != 0 || s->H % 64 != 0 || s->H > ((int64_t)1 << 22)) return UBEP_ERR_UNSUPPORTED;
     if (!aligned(x, 16) || !aligned(w, 16) || !aligned(y, 16) || !aligned(ws, 256) ||
         !aligned(expert_offset, 4))
         return UBEP_ERR_INVALID_ARG;
@@ -333,6 +333,16 @@ ubep_status ubep_expert_linear(const ubep_shape* s, int64_t N, const int32_t* ex
         return UBEP_ERR_UNSUPPORTED;
     uint32_t* status = static_cast<uint32_t*>(ws) + kHdrStatus;
     return hip_status(launch_expert_linear(s->E, s->H, N, rows, expert_offset, x, w, y, status, stream));
+}
+
+ubep_status ubep_expert_pack_weights(int32_t E, int64_t N, int64_t H, const void* w, void* packed,
+                                     hipStream_t stream) {
+    if (!w || !packed || E <= 0 || N <= 0 || H <= 0) return UBEP_ERR_INVALID_ARG;
+    if (N % 128 != 0 || H % 64 != 0 || H > ((int64_t)1 << 22) || E > kExpertMaxE)
+        return UBEP_ERR_UNSUPPORTED;
+    if (!aligned(w, 16) || !aligned(packed, 16) || w == packed) return UBEP_ERR_INVALID_ARG;
+    if ((int64_t)E * N * H / 8 / 256 >= ((int64_t)1 << 32)) return UBEP_ERR_UNSUPPORTED;
+    return hip_status(launch_expert_pack(E, N, H, w, packed, stream));
 }
 
 ubep_status ubep_get_device_status(void* ws, size_t ws_bytes, hipStream_t stream,

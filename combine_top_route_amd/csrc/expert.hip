@@ -5,6 +5,12 @@
 //
 //   y[r][n] = bf16( sum over c of x[r][c] * w[e][n][c] )   for r in expert e's run
 //
+// The weights come packed (expert_pack_kernel): each k step of an output tile
+// reads one contiguous 16 KB block, so the weight stream, the bulk of the
+// bytes when few rows reach each expert, is sequential per workgroup instead
+// of 128 rows read 128 bytes at a time (scattered rows thrash the HBM row
+// buffers: half the bandwidth).
+//
 // A dense contraction per expert, so it runs on the matrix cores:
 // v_mfma_f32_16x16x32_bf16 (gfx950) with fp32 accumulation.  A workgroup of
 // 4 waves computes a 128 (output channels) x 128 (rows) tile of one expert;
@@ -12,8 +18,8 @@
 // MFMA's A operand and the receive rows its B operand, both read as 16-byte
 // runs of 8 channels, so each lane's 4 accumulator values are 4 consecutive
 // output channels of one row (one 8-byte store).  k steps of 64 channels are
-// staged through LDS (rows padded by 16 bytes), and the next step's global
-// loads are in flight while the current step's MFMAs run.
+// staged through LDS (rows padded by 32 bytes), and the next two steps'
+// global loads are in flight while the current step's MFMAs run.
 //
 // Tiles: blockIdx.x is the output-channel tile, blockIdx.y a row tile counted
 // over all experts in expert order (expert e owns ceil(count_e / 128) of
@@ -34,16 +40,16 @@ constexpr int kGemmThreads = 256;
 constexpr int kBN = 128;                 // output channels per tile
 constexpr int kBM = 128;                 // rows per tile
 constexpr int kBK = 64;                  // channels per k step
-constexpr int kLdsStride = kBK + 8;      // bf16 per LDS row: 144 bytes
+constexpr int kLdsStride = kBK + 16;     // bf16 per LDS row: 160 bytes (fewest bank conflicts measured)
 constexpr int kPerThreadE = kExpertMaxE / kGemmThreads;
 constexpr int kVecPerRow = kBK / 8;                          // 16-byte vectors per tile row
-constexpr int kLoadsPerThread = kBM * kVecPerRow / kGemmThreads;
-static_assert(kBM == kBN, "one load mapping serves both tiles");
+constexpr int kLoadsW = kBN * kVecPerRow / kGemmThreads;     // weight vectors per thread and step
+constexpr int kLoadsX = kBM * kVecPerRow / kGemmThreads;     // receive-row vectors per thread and step
 
 struct ExpertArgs {
     const int32_t* eoff;     // [E+1]
     const u32x4* x;          // [n_rows][H/8]
-    const u32x4* w;          // [E][N][H/8]
+    const u32x4* w;          // packed [E][N/128][H/64][128][64 / 8]
     uint2* y;                // [n_rows][N/4]
     uint32_t* status;
     int64_t H, N, n_rows;
@@ -57,7 +63,7 @@ __device__ __forceinline__ uint2 pack_bf16x4(f32x4 v) {
     return o;
 }
 
-__global__ __launch_bounds__(kGemmThreads) void expert_linear_kernel(ExpertArgs a) {
+__global__ __launch_bounds__(kGemmThreads, 2) void expert_linear_kernel(ExpertArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t s_w[kBN * kLdsStride];
     __shared__ __attribute__((aligned(16))) uint16_t s_x[kBM * kLdsStride];
     __shared__ int32_t s_wsum[kGemmThreads / 64];
@@ -111,19 +117,49 @@ __global__ __launch_bounds__(kGemmThreads) void expert_linear_kernel(ExpertArgs 
     const int64_t r_lo = run_lo + (int64_t)s_sel[1] * kBM;
 
     // ---- k loop
+    // Buffer resources over the tile's 128 weight rows and its receive rows
+    // (at most 128; loads past the run's end read zeros).  Each lane's row and
+    // vector offset stays in one VGPR per load; the k step is a scalar offset.
     const int64_t nvh = a.H / 8;
-    const u32x4* wt = a.w + ((int64_t)e * a.N + n0) * nvh;
-    const u32x4 zero = {0u, 0u, 0u, 0u};
-    u32x4 pw[kLoadsPerThread], px[kLoadsPerThread];
-    auto load_step = [&](int64_t kv) {                   // kv: 16-byte vector offset of the step
+    const int32_t row_bytes = (int32_t)(a.H * 2);
+    const int64_t n_x = r_end - r_lo < kBM ? r_end - r_lo : kBM;
+    // packed weights: the (expert, output tile) block holds the tile's k steps
+    // back to back, each a row-major 128 x 64 bf16 block of 16 KB
+    const int64_t n_ksteps = a.H / kBK;
+    const u32x4* wblk = a.w + ((int64_t)e * (a.N / kBN) + blockIdx.x) * n_ksteps * (kBN * kVecPerRow);
+    const __amdgpu_buffer_rsrc_t rw = row_rsrc(wblk, n_ksteps * kBN * kBK * 2);
+    const __amdgpu_buffer_rsrc_t rx = row_rsrc(a.x + r_lo * nvh, n_x * row_bytes);
+    // two k steps of global loads in flight: while step kt's fragments are
+    // multiplied, the loads of steps kt+1 and kt+2 are outstanding
+    u32x4 pw0[kLoadsW], px0[kLoadsX], pw1[kLoadsW], px1[kLoadsX];
+    int32_t xoff[kLoadsX];
 #pragma unroll
-        for (int i = 0; i < kLoadsPerThread; ++i) {
-            const int q = tid + kGemmThreads * i;        // 128 rows x kVecPerRow vectors
-            const int row = q / kVecPerRow, cv = q % kVecPerRow;
-            pw[i] = wt[(int64_t)row * nvh + kv + cv];
-            const int64_t r = r_lo + row;
-            px[i] = r < r_end ? a.x[r * nvh + kv + cv] : zero;
+    for (int i = 0; i < kLoadsX; ++i) {
+        const int q = tid + kGemmThreads * i;            // kBM rows x kVecPerRow vectors
+        xoff[i] = (q / kVecPerRow) * row_bytes + (q % kVecPerRow) * 16;
+    }
+    auto load_step = [&](int64_t kt, u32x4 (&dw)[kLoadsW], u32x4 (&dx)[kLoadsX]) {
+        const int32_t wso = (int32_t)(kt * (kBN * kBK * 2)), xso = (int32_t)(kt * (kBK * 2));
+#pragma unroll
+        for (int i = 0; i < kLoadsW; ++i)   // weights: one contiguous 16 KB block per step
+            dw[i] = __builtin_amdgcn_raw_buffer_load_b128(rw, (tid + kGemmThreads * i) * 16, wso, 0);
+#pragma unroll
+        for (int i = 0; i < kLoadsX; ++i)
+            dx[i] = __builtin_amdgcn_raw_buffer_load_b128(rx, xoff[i], xso, 0);
+    };
+    auto stage = [&](const u32x4 (&sw)[kLoadsW], const u32x4 (&sx)[kLoadsX]) {
+        __syncthreads();                                 // the last step's fragments are read
+#pragma unroll
+        for (int i = 0; i < kLoadsW; ++i) {
+            const int q = tid + kGemmThreads * i;
+            *reinterpret_cast<u32x4*>(&s_w[(q / kVecPerRow) * kLdsStride + (q % kVecPerRow) * 8]) = sw[i];
         }
+#pragma unroll
+        for (int i = 0; i < kLoadsX; ++i) {
+            const int q = tid + kGemmThreads * i;
+            *reinterpret_cast<u32x4*>(&s_x[(q / kVecPerRow) * kLdsStride + (q % kVecPerRow) * 8]) = sx[i];
+        }
+        __syncthreads();
     };
     f32x4 acc[4][4];
 #pragma unroll
@@ -133,19 +169,7 @@ __global__ __launch_bounds__(kGemmThreads) void expert_linear_kernel(ExpertArgs 
 
     const int wn = (wave & 1) * 64, wm = (wave >> 1) * 64;
     const int fr = lane & 15, fk = (lane >> 4) * 8;      // fragment row and channel offset
-    const int64_t nk = a.H / kBK;
-    load_step(0);
-    for (int64_t kt = 0; kt < nk; ++kt) {
-        __syncthreads();                                 // the last step's fragments are read
-#pragma unroll
-        for (int i = 0; i < kLoadsPerThread; ++i) {
-            const int q = tid + kGemmThreads * i;
-            const int row = q / kVecPerRow, cv = q % kVecPerRow;
-            *reinterpret_cast<u32x4*>(&s_w[row * kLdsStride + cv * 8]) = pw[i];
-            *reinterpret_cast<u32x4*>(&s_x[row * kLdsStride + cv * 8]) = px[i];
-        }
-        __syncthreads();
-        if (kt + 1 < nk) load_step((kt + 1) * (kBK / 8)); // next step's loads overlap the MFMAs
+    auto multiply = [&]() {
 #pragma unroll
         for (int ks = 0; ks < kBK; ks += 32) {
             bf16x8 fa[4], fb[4];
@@ -160,6 +184,18 @@ __global__ __launch_bounds__(kGemmThreads) void expert_linear_kernel(ExpertArgs 
                 for (int j = 0; j < 4; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
         }
+    };
+    const int64_t nk = n_ksteps;
+    load_step(0, pw0, px0);
+    if (nk > 1) load_step(1, pw1, px1);
+    for (int64_t kt = 0; kt < nk; kt += 2) {
+        stage(pw0, px0);
+        if (kt + 2 < nk) load_step(kt + 2, pw0, px0);
+        multiply();
+        if (kt + 1 >= nk) break;
+        stage(pw1, px1);
+        if (kt + 3 < nk) load_step(kt + 3, pw1, px1);
+        multiply();
     }
 
     // ---- epilogue: lane holds channels n .. n+3 of row r for each (i, j)
@@ -174,6 +210,31 @@ __global__ __launch_bounds__(kGemmThreads) void expert_linear_kernel(ExpertArgs 
             a.y[r * nq + n / 4] = pack_bf16x4(acc[i][j]);
         }
     }
+}
+
+// packed[e][nt][kt][r][c] = w[e][nt*128 + r][kt*64 + c]: every 128 x 64 block
+// that one k step of one output tile reads becomes 16 contiguous KB.  One
+// thread moves one 16-byte vector (8 channels).
+__global__ __launch_bounds__(256) void expert_pack_kernel(const u32x4* __restrict__ w,
+                                                          u32x4* __restrict__ packed, int64_t N,
+                                                          int64_t H, int64_t total) {
+    const int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;   // packed vector index
+    if (v >= total) return;
+    const int64_t vpb = kBN * kVecPerRow;                // vectors per 128 x 64 block
+    const int64_t blk = v / vpb, in = v % vpb;
+    const int64_t r = in / kVecPerRow, cv = in % kVecPerRow;
+    const int64_t ksteps = H / kBK, ntiles = N / kBN;
+    const int64_t kt = blk % ksteps, nt = (blk / ksteps) % ntiles, e = blk / (ksteps * ntiles);
+    const int64_t n = nt * kBN + r;
+    packed[v] = w[(e * N + n) * (H / 8) + kt * kVecPerRow + cv];
+}
+
+hipError_t launch_expert_pack(int32_t E, int64_t N, int64_t H, const void* w, void* packed,
+                              hipStream_t stream) {
+    const int64_t total = (int64_t)E * N * H / 8;
+    const int64_t blocks = (total + 255) / 256;
+    return launch_kernel(expert_pack_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                         static_cast<const u32x4*>(w), static_cast<u32x4*>(packed), N, H, total);
 }
 
 hipError_t launch_expert_linear(int32_t E, int64_t H, int64_t N, int64_t n_rows,

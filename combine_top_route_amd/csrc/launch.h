@@ -80,6 +80,9 @@ hipError_t launch_expert_linear(int32_t E, int64_t H, int64_t N, int64_t n_rows,
                                 const int32_t* expert_offset, const void* x, const void* w, void* y,
                                 uint32_t* status, hipStream_t stream);
 
+hipError_t launch_expert_pack(int32_t E, int64_t N, int64_t H, const void* w, void* packed,
+                              hipStream_t stream);
+
 hipError_t launch_identity_fp8(int64_t rows, int64_t H, const uint8_t* q, const float* scale,
                                void* y, hipStream_t stream);
 

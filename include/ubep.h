@@ -291,17 +291,28 @@ ubep_status ubep_recv_sentinel_init(void *recv, int64_t rows, int64_t H, hipStre
  * with bf16 products accumulated in fp32 on the matrix cores (the order of
  * the accumulation is the hardware's) and one round to nearest even.
  * x: bf16 [T*k][H], rows in the order of ubep_layout_grouped (its pos and
- * expert_offset); w: bf16 [E][N][H] (row n of expert e's weight, channels
- * contiguous); y: bf16 [T*k][N] (with N = H it is combine's input).
+ * expert_offset); w: the weights bf16 [E][N][H] (row n of expert e's weight,
+ * channels contiguous) in the packed order of ubep_expert_pack_weights;
+ * y: bf16 [T*k][N] (with N = H it is combine's input).
  * expert_offset: int32 [E+1] device array, non-decreasing from 0 to at most
  * T*k (ubep_layout_grouped's output); rows outside every run are not written.
- * Limits: H % 64 == 0, N % 128 == 0, E <= 1024, ceil(T*k/128) + E <= 65535
+ * Limits: H % 64 == 0, H <= 2^22, N % 128 == 0, E <= 1024, ceil(T*k/128) + E <= 65535
  * (else UBEP_ERR_UNSUPPORTED).  An offset outside [0, T*k] sets
  * UBEP_ERR_BAD_POSITION and that expert's rows are skipped.  The workspace
  * is used for the status word only.  One kernel on `stream`. */
 ubep_status ubep_expert_linear(const ubep_shape *shape /*host*/, int64_t N,
                                const int32_t *expert_offset, const void *x, const void *w,
                                void *y, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Repack expert weights for ubep_expert_linear (once, when the weights are
+ * loaded): w bf16 [E][N][H] -> packed bf16 of the same size, where block
+ * (e, n/128, c/64) of 128 x 64 values is stored contiguously, row-major:
+ *   packed[((e*(N/128) + n/128)*(H/64) + c/64)*8192 + (n%128)*64 + c%64] = w[e][n][c].
+ * A bit permutation: each k step of an output tile of the expert kernel then
+ * reads 16 contiguous KB.  w and packed must not overlap.  Limits as
+ * ubep_expert_linear.  One kernel on `stream`. */
+ubep_status ubep_expert_pack_weights(int32_t E, int64_t N, int64_t H, const void *w, void *packed,
+                                     hipStream_t stream);
 
 /* Synchronise `stream`, read the device status word into *out (host) and
  * clear it.  Returns UBEP_OK if the read itself succeeded. */

@@ -164,3 +164,11 @@ def test_expert_linear_validation_without_gpu():
     big = ubep.ubep_shape(2048, 128, 2048, 2, 2, 1)
     assert L.ubep_expert_linear(C.byref(big), 128, 256, 256, 256, 256, 256, 4096,
                                 None) == ubep.ERR_UNSUPPORTED           # E > 1024
+
+
+def test_expert_pack_validation_without_gpu():
+    L = ubep.lib()
+    assert L.ubep_expert_pack_weights(2, 100, 128, 256, 512, None) == ubep.ERR_UNSUPPORTED   # N
+    assert L.ubep_expert_pack_weights(2, 128, 96, 256, 512, None) == ubep.ERR_UNSUPPORTED    # H
+    assert L.ubep_expert_pack_weights(2, 128, 128, 256, 256, None) == ubep.ERR_INVALID_ARG   # in place
+    assert L.ubep_expert_pack_weights(0, 128, 128, 256, 512, None) == ubep.ERR_INVALID_ARG

@@ -45,6 +45,21 @@ def _weights(E, N, H, seed, scale):
     return (torch.randn((E, N, H), generator=g, device="cuda") * scale).to(torch.bfloat16)
 
 
+def _packed(W):
+    E, N, H = W.shape
+    P = torch.empty_like(W)
+    ubep.ubep_expert_pack_weights(E, N, H, W, P)
+    return P
+
+
+def test_pack_weights_is_the_block_permutation():
+    E, N, H = 3, 256, 192
+    W = _weights(E, N, H, 60, 1.0)
+    got = _bits(_packed(W))
+    want = _bits(W).reshape(E, N // 128, 128, H // 64, 64).transpose(0, 1, 3, 2, 4).ravel()
+    np.testing.assert_array_equal(got.ravel(), want)
+
+
 def _check_rows(x_bits, w_bits, e_of_row, y_gpu, y_ref):
     """Per-element bound above on the rows given (x_bits [n, H], w_bits the
     weights of each row's expert via e_of_row)."""
@@ -82,7 +97,7 @@ def test_expert_linear_matches_oracle(spec):
     ubep.ubep_dispatch(b.shape, ubep.BF16, b.x, b.pos, b.recv, None, b.ws)
     W = _weights(s.E, N, s.H, spec["seed"], 0.05)
     y = torch.empty((s.T * s.k, N), dtype=torch.bfloat16, device="cuda")
-    ubep.ubep_expert_linear(b.shape, N, eoff, b.recv, W, y, b.ws)
+    ubep.ubep_expert_linear(b.shape, N, eoff, b.recv, _packed(W), y, b.ws)
     torch.cuda.synchronize()
     assert device_status(b) == ubep.OK
     off = to_np(eoff)
@@ -102,7 +117,7 @@ def test_identity_weights_are_bit_exact():
     ubep.ubep_dispatch(b.shape, ubep.BF16, b.x, b.pos, b.recv, None, b.ws)
     W = torch.eye(s.H, device="cuda", dtype=torch.bfloat16).expand(s.E, -1, -1).contiguous()
     y = torch.full((s.T * s.k, s.H), 7.0, dtype=torch.bfloat16, device="cuda")
-    ubep.ubep_expert_linear(b.shape, s.H, eoff, b.recv, W, y, b.ws)
+    ubep.ubep_expert_linear(b.shape, s.H, eoff, b.recv, _packed(W), y, b.ws)
     torch.cuda.synchronize()
     assert device_status(b) == ubep.OK
     assert torch.equal(y.view(torch.int16), b.recv.view(torch.int16))
@@ -119,7 +134,7 @@ def test_moe_layer_end_to_end():
     ubep.ubep_dispatch(b.shape, ubep.BF16, b.x, b.pos, b.recv, None, b.ws)
     W = _weights(s.E, s.H, s.H, 66, 0.04)
     y = torch.empty((s.T * s.k, s.H), dtype=torch.bfloat16, device="cuda")
-    ubep.ubep_expert_linear(b.shape, s.H, eoff, b.recv, W, y, b.ws)
+    ubep.ubep_expert_linear(b.shape, s.H, eoff, b.recv, _packed(W), y, b.ws)
     ubep.ubep_combine(b.shape, y, b.pos, b.topk_w, b.out, b.ws)
     torch.cuda.synchronize()
     assert device_status(b) == ubep.OK
@@ -147,7 +162,7 @@ def test_expert_linear_full_depth_sampled():
     ubep.ubep_dispatch(b.shape, ubep.BF16, b.x, b.pos, b.recv, None, b.ws)
     W = _weights(s.E, N, s.H, 67, 0.02)
     y = torch.empty((s.T * s.k, N), dtype=torch.bfloat16, device="cuda")
-    ubep.ubep_expert_linear(b.shape, N, eoff, b.recv, W, y, b.ws)
+    ubep.ubep_expert_linear(b.shape, N, eoff, b.recv, _packed(W), y, b.ws)
     torch.cuda.synchronize()
     assert device_status(b) == ubep.OK
     off = to_np(eoff)
