@@ -121,3 +121,25 @@ def test_grouped_bad_expert_id_reported(T):
     got = _grouped(b)
     assert device_status(b) == ubep.ERR_BAD_EXPERT_ID
     assert np.all((got["pos"] >= 0) & (got["pos"] < T * 4))
+
+
+@pytest.mark.parametrize("pipeline", ["chunked", "sentinel"])
+def test_pipelines_take_grouped_positions(pipeline):
+    """The one-launch pipelines move rows by pos, whatever its order: with the
+    expert-grouped layout they give the oracle's combine bit for bit."""
+    w = custom(T=2048, H=512, E=64, k=6, R=8, C=4, routing="zipf", weights="softmax", seed=42)
+    s = w.shape
+    say(f"grouped positions through the {pipeline} pipeline")
+    b = upload(w)
+    _grouped(b)
+    if pipeline == "chunked":
+        ubep.ubep_dispatch_combine_chunked(b.shape, b.x, b.pos, b.topk_w, b.recv, b.out,
+                                           [3, 1, 0, 2], b.ws)
+    else:
+        ubep.ubep_recv_sentinel_init(b.recv, s.T * s.k, s.H)
+        ubep.ubep_dispatch_combine_sentinel(b.shape, b.x, b.pos, b.topk_w, b.recv, b.out, b.ws)
+    torch.cuda.synchronize()
+    assert device_status(b) == ubep.OK
+    L = oracle.layout_grouped(w.topk_idx, s.E, s.R, s.C)
+    recv = oracle.dispatch_bf16(w.x, L["pos"])
+    np.testing.assert_array_equal(to_np(b.out), oracle.combine(recv, L["pos"], w.topk_w))
