@@ -39,7 +39,10 @@ hipError_t launch_combine(const Plan& p, const void* y, const int32_t* pos, cons
         const hipError_t e = resident_blocks(reinterpret_cast<const void*>(combine_kernel<GG, VV>),
                                              kCombineBlock, 0, &n_static);
         if (e != hipSuccess) return e;
-        if (n_static > blocks) n_static = blocks;
+        // start-order tickets only when later workgroups are many more than
+        // the first resident wave (long grids drift apart across XCDs); with
+        // a grid of a few waves they cost more than they save
+        if (blocks < kTicketMinWaves * n_static) n_static = blocks;
         return launch_kernel(combine_kernel<GG, VV>, dim3((unsigned)blocks), dim3(kCombineBlock), 0,
                              stream, static_cast<const u32x4*>(y), pos, topk_w,
                              static_cast<u32x4*>(out), p.T, p.k, p.H / 8, p.rows, status,

@@ -51,7 +51,10 @@ hipError_t launch_dispatch_bf16(const Plan& p, const void* x, const int32_t* pos
         const hipError_t e = resident_blocks(
             reinterpret_cast<const void*>(dispatch_bf16_kernel<GG, VV, false>), kRowBlock, 0, &n_static);
         if (e != hipSuccess) return e;
-        if (n_static > blocks) n_static = blocks;
+        // start-order tickets only when later workgroups are many more than
+        // the first resident wave (long grids drift apart across XCDs); with
+        // a grid of a few waves they cost more than they save
+        if (blocks < kTicketMinWaves * n_static) n_static = blocks;
         return launch_kernel(dispatch_bf16_kernel<GG, VV, false>, dim3((unsigned)blocks),
                              dim3(kRowBlock), 0, stream, static_cast<const u32x4*>(x), pos,
                              static_cast<u32x4*>(recv), p.T, p.k, p.H / 8, p.rows, status,

@@ -96,6 +96,10 @@ hipError_t launch_clear_status(uint32_t* status, hipStream_t stream);
 // the current device at once: blocks per CU times CUs (cached per kernel).
 hipError_t resident_blocks(const void* kernel, int block, size_t lds, int64_t* out);
 
+// Grids of fewer than this many resident waves of workgroups hand out token
+// blocks by workgroup index alone (no start-order tickets).
+constexpr int64_t kTicketMinWaves = 8;
+
 // Device properties used to size persistent grids and bounded waits.
 struct DeviceInfo {
     int cus;

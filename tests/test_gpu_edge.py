@@ -226,10 +226,11 @@ def _exact_path(w, b):
 
 def test_block_tickets_reset_across_grids():
     """Dispatch and combine hand their later workgroups token blocks from
-    ticket counters in the workspace; grids larger than the chip holds use
-    them, and alternating grid sizes on one workspace must stay exact."""
-    shapes = [dict(T=16384, H=64, E=64, k=4, R=16), dict(T=12288, H=128, E=32, k=4, R=8),
-              dict(T=16384, H=64, E=64, k=4, R=16)]
+    ticket counters in the workspace; grids of at least eight times the
+    workgroups the chip holds at once use them (65536 tokens of 4 per
+    workgroup), and alternating grid sizes on one workspace must stay exact."""
+    shapes = [dict(T=65536, H=64, E=64, k=4, R=16), dict(T=98304, H=128, E=32, k=4, R=8),
+              dict(T=65536, H=64, E=64, k=4, R=16)]
     nws = max(ubep.ubep_workspace_bytes(dict(C=1, **s)) for s in shapes)
     ws = torch.zeros(nws, dtype=torch.uint8, device="cuda")
     for i, sh in enumerate(shapes):
@@ -241,7 +242,7 @@ def test_block_tickets_reset_across_grids():
 
 
 def test_stale_block_ticket_is_reported_and_init_recovers():
-    w = custom(T=16384, H=64, E=64, k=4, R=16, seed=60)
+    w = custom(T=65536, H=64, E=64, k=4, R=16, seed=60)
     b = upload(w)
     s = w.shape.as_dict()
     ubep.ubep_layout(s, b.topk_idx, b.pos, b.expert_count, b.rank_count, b.recv_offset,
