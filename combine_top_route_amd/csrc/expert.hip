@@ -18,7 +18,7 @@
 // MFMA's A operand and the receive rows its B operand, both read as 16-byte
 // runs of 8 channels, so each lane's 4 accumulator values are 4 consecutive
 // output channels of one row (one 8-byte store).  k steps of 64 channels are
-// staged through LDS (rows padded by 32 bytes), and the next two steps'
+// staged through LDS (16-byte units swizzled per row pair), and the next two steps'
 // global loads are in flight while the current step's MFMAs run.
 //
 // Tiles: blockIdx.x is the output-channel tile, blockIdx.y a row tile counted
@@ -40,7 +40,14 @@ constexpr int kGemmThreads = 256;
 constexpr int kBN = 128;                 // output channels per tile
 constexpr int kBM = 128;                 // rows per tile
 constexpr int kBK = 64;                  // channels per k step
-constexpr int kLdsStride = kBK + 16;     // bf16 per LDS row: 160 bytes (fewest bank conflicts measured)
+constexpr int kLdsStride = kBK;          // bf16 per LDS row: 128 bytes, 16-byte units swizzled
+static_assert(kBK == 64, "the LDS swizzle permutes the 8 units of a 64-channel row");
+
+// LDS element offset of 16-byte unit u of tile row r.  Rows are 128 bytes, so
+// an even and an odd row together span the 64 banks; unit u of row r sits at
+// position u ^ ((r / 2) % 8).  A quarter wave's stores (two rows) and its
+// fragment loads (16 rows at one unit) then each touch every bank once.
+__device__ __forceinline__ int lds_at(int r, int u) { return r * kLdsStride + ((u ^ ((r >> 1) & 7)) << 3); }
 constexpr int kPerThreadE = kExpertMaxE / kGemmThreads;
 constexpr int kVecPerRow = kBK / 8;                          // 16-byte vectors per tile row
 constexpr int kLoadsW = kBN * kVecPerRow / kGemmThreads;     // weight vectors per thread and step
@@ -152,12 +159,12 @@ __global__ __launch_bounds__(kGemmThreads, 2) void expert_linear_kernel(ExpertAr
 #pragma unroll
         for (int i = 0; i < kLoadsW; ++i) {
             const int q = tid + kGemmThreads * i;
-            *reinterpret_cast<u32x4*>(&s_w[(q / kVecPerRow) * kLdsStride + (q % kVecPerRow) * 8]) = sw[i];
+            *reinterpret_cast<u32x4*>(&s_w[lds_at(q / kVecPerRow, q % kVecPerRow)]) = sw[i];
         }
 #pragma unroll
         for (int i = 0; i < kLoadsX; ++i) {
             const int q = tid + kGemmThreads * i;
-            *reinterpret_cast<u32x4*>(&s_x[(q / kVecPerRow) * kLdsStride + (q % kVecPerRow) * 8]) = sx[i];
+            *reinterpret_cast<u32x4*>(&s_x[lds_at(q / kVecPerRow, q % kVecPerRow)]) = sx[i];
         }
         __syncthreads();
     };
@@ -175,8 +182,8 @@ __global__ __launch_bounds__(kGemmThreads, 2) void expert_linear_kernel(ExpertAr
             bf16x8 fa[4], fb[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                fa[i] = *reinterpret_cast<const bf16x8*>(&s_w[(wn + 16 * i + fr) * kLdsStride + ks + fk]);
-                fb[i] = *reinterpret_cast<const bf16x8*>(&s_x[(wm + 16 * i + fr) * kLdsStride + ks + fk]);
+                fa[i] = *reinterpret_cast<const bf16x8*>(&s_w[lds_at(wn + 16 * i + fr, (ks + fk) >> 3)]);
+                fb[i] = *reinterpret_cast<const bf16x8*>(&s_x[lds_at(wm + 16 * i + fr, (ks + fk) >> 3)]);
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i)
