@@ -180,3 +180,30 @@ def test_expert_linear_full_depth_sampled():
         sub_off = np.array([0, len(rows)], np.int32)
         ref = oracle.expert_linear(xr, we, sub_off)
         _check_rows(xr, we, np.zeros(len(rows), int), _bits(y[torch.from_numpy(rows).cuda()]), ref)
+
+
+def test_bad_expert_offsets_reported_and_skipped():
+    """An offset past T*k is reported; that expert's rows are skipped and the
+    others are computed as usual."""
+    w = custom(T=256, H=128, E=8, k=2, R=2, C=1, routing="topk", weights="softmax", seed=68)
+    s = w.shape
+    say("expert linear bad offsets")
+    b = upload(w)
+    eoff = _grouped_layout(b)
+    ubep.ubep_dispatch(b.shape, ubep.BF16, b.x, b.pos, b.recv, None, b.ws)
+    torch.cuda.synchronize()
+    good = to_np(eoff).copy()
+    bad = good.copy()
+    bad[8] = s.T * s.k + 1000                       # expert 7 ends past the receive rows
+    eb = torch.from_numpy(bad).cuda()
+    W = _weights(s.E, 128, s.H, 68, 0.05)
+    y = torch.zeros((s.T * s.k, 128), dtype=torch.bfloat16, device="cuda")
+    ubep.ubep_expert_linear(b.shape, 128, eb, b.recv, _packed(W), y, b.ws)
+    torch.cuda.synchronize()
+    assert device_status(b) == ubep.ERR_BAD_POSITION
+    xr, wb = _bits(b.recv), _bits(W)
+    lo = good[7]
+    ref = oracle.expert_linear(xr[:lo], wb[:7], good[:8])
+    e_of_row = np.repeat(np.arange(7), np.diff(good[:8]))
+    _check_rows(xr[:lo], wb, e_of_row, _bits(y[:lo]), ref)
+    assert not bool(y[lo:].view(torch.int16).any())  # expert 7's rows untouched
