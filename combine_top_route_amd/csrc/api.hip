@@ -272,7 +272,7 @@ ubep_status ubep_dispatch_combine_chunked(const ubep_shape* s, const void* x, co
     if (!x || !pos || !topk_w || !recv || !out || !ws) return UBEP_ERR_INVALID_ARG;
     if (ws_bytes < p.ws_bytes || !aligned(ws, 256)) return UBEP_ERR_INVALID_ARG;
     if (!aligned(x, 16) || !aligned(recv, 16) || !aligned(out, 16)) return UBEP_ERR_INVALID_ARG;
-    if (debug_flags & ~1u) return UBEP_ERR_INVALID_ARG;
+    if (debug_flags & ~3u) return UBEP_ERR_INVALID_ARG;
     if (chunk_order != nullptr) {
         bool seen[kMaxC] = {};
         for (int32_t i = 0; i < p.C; ++i) {
@@ -300,7 +300,7 @@ ubep_status ubep_dispatch_combine_sentinel(const ubep_shape* s, const void* x, c
     if (!x || !pos || !topk_w || !recv || !out || !ws || ws_bytes < kHdrBytes) return UBEP_ERR_INVALID_ARG;
     if (!aligned(x, 16) || !aligned(recv, 16) || !aligned(out, 16) || !aligned(ws, 256))
         return UBEP_ERR_INVALID_ARG;
-    if (debug_flags & ~1u) return UBEP_ERR_INVALID_ARG;
+    if (debug_flags & ~3u) return UBEP_ERR_INVALID_ARG;
     uint64_t ticks;
     const ubep_status ts = spin_ticks_for(spin_limit_ns, &ticks);
     if (ts != UBEP_OK) return ts;

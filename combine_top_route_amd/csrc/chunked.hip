@@ -20,8 +20,9 @@
 // Every D task of chunk c has a smaller ticket than every C task of chunk c,
 // and D tasks never wait, so each awaited task is already held by a running
 // workgroup: the pipeline cannot deadlock whatever the grid size.  Waits are
-// bounded by a clock limit; an expired wait records UBEP_ERR_TIMEOUT and
-// moves on, so every workgroup always reaches the exit.  The last workgroup
+// bounded by a clock limit; an expired wait records UBEP_ERR_TIMEOUT, sets a
+// give-up word that ends every later wait at once, and moves on, so every
+// workgroup always reaches the exit.  The last workgroup
 // to leave resets the ticket and the flags for the next call.
 #include "launch.h"
 #include "rows.h"
@@ -109,12 +110,14 @@ __global__ __launch_bounds__(kChunkBlock) void chunked_kernel(ChunkArgs a) {
                                                        gtid, status);
             wait_memory();             // every row of the task is at the coherent level
             __syncthreads();
-            if (tid == 0 && (a.debug & 1u) == 0u) add_relaxed(flag, 1u);
+            if ((a.debug & kDebugDelay) != 0u && idx % 3u == 0u) debug_delay();
+            if (tid == 0 && (a.debug & kDebugWithhold) == 0u) add_relaxed(flag, 1u);
         } else {
             if (tid == 0) {
                 const uint64_t t0 = now_ticks();
                 while (ld_relaxed(flag) < n) {
-                    if (now_ticks() - t0 > a.spin_ticks) {
+                    if (now_ticks() - t0 > a.spin_ticks || ld_relaxed(&a.hdr[kHdrFusedGiveUp]) != 0u) {
+                        st_relaxed(&a.hdr[kHdrFusedGiveUp], 1u);
                         raise_status(status, UBEP_ERR_TIMEOUT);
                         break;
                     }
@@ -134,6 +137,7 @@ __global__ __launch_bounds__(kChunkBlock) void chunked_kernel(ChunkArgs a) {
         if (done == gridDim.x - 1u) {
             for (int32_t c = 0; c < a.C; ++c) st_relaxed(a.flags + (int64_t)c * kFlagStride, 0u);
             st_relaxed(&a.hdr[kHdrFusedTicket], 0u);
+            st_relaxed(&a.hdr[kHdrFusedGiveUp], 0u);
             st_relaxed(&a.hdr[kHdrFusedDone], 0u);
         }
     }

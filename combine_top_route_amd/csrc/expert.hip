@@ -81,19 +81,26 @@ __global__ __launch_bounds__(kGemmThreads, 2) void expert_linear_kernel(ExpertAr
     const int64_t n0 = (int64_t)blockIdx.x * kBN;
 
     // ---- which expert and which of its row tiles this workgroup takes
+    // offsets must run non-decreasing from 0 within [0, n_rows]; an expert
+    // whose run is reversed gets no tiles, and workgroup (0, 0) reports any
+    // violation (the tiles are then no longer sure to cover every run)
     int32_t cnt[kPerThreadE];
     int32_t mine = 0;
+    bool bad_off = false;
 #pragma unroll
     for (int i = 0; i < kPerThreadE; ++i) {
         const int32_t e = tid * kPerThreadE + i;
         int32_t c = 0;
         if (e < a.E) {
-            const int32_t rows = a.eoff[e + 1] - a.eoff[e];
+            const int32_t lo = a.eoff[e], hi = a.eoff[e + 1];
+            const int32_t rows = hi - lo;
+            if (rows < 0 || lo < 0 || (int64_t)hi > a.n_rows || (e == 0 && lo != 0)) bad_off = true;
             c = rows > 0 ? (rows + kBM - 1) / kBM : 0;
         }
         cnt[i] = c;
         mine += c;
     }
+    if (bad_off && blockIdx.x == 0 && blockIdx.y == 0) raise_status(a.status, UBEP_ERR_BAD_POSITION);
     int32_t inc = mine;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {

@@ -39,6 +39,8 @@ constexpr int kHdrDispatchTicket = 288; // block ticket of the dispatch's later 
 constexpr int kHdrFusedBlockTicket = 320; // block ticket of the fused launch's later workgroups
 constexpr int kHdrSentTicket = 352;    // task ticket of the sentinel-readiness pipeline
 constexpr int kHdrSentDone = 384;      // workgroups finished in the sentinel-readiness pipeline
+constexpr int kHdrSentGiveUp = 416;    // set once a sentinel wait has expired: later waits give up
+constexpr int kHdrFusedGiveUp = 448;   // set once a chunk-flag wait has expired: later waits give up
 constexpr size_t kHdrBytes = 2048;
 // Readiness sentinel of the sentinel-polling pipeline: every 32-bit word of a
 // receive row's first 16-byte unit while the row is empty (two bf16 NaNs).

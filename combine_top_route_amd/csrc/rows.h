@@ -93,6 +93,16 @@ __device__ __forceinline__ void wait_memory() {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
+// Debug aid of the pipelines (debug flag bit 1): hold a producer back for
+// about 25 us before it publishes, so that consumers find their data late.
+// A fixed number of sleeps: it always ends.
+constexpr uint32_t kDebugWithhold = 1u;   // bit 0: never publish (forces the time-out path)
+constexpr uint32_t kDebugDelay = 2u;      // bit 1: publish late
+__device__ __forceinline__ void debug_delay() {
+#pragma unroll 1
+    for (int i = 0; i < 8; ++i) __builtin_amdgcn_s_sleep(127);
+}
+
 __device__ __forceinline__ bool row_ok(int32_t q, int64_t n_rows) {
     return (uint64_t)(int64_t)q < (uint64_t)n_rows;
 }

@@ -26,8 +26,11 @@
 // and a C task waits only on the D task of the same block, which has a
 // smaller ticket and never waits: every awaited task is held by a running
 // workgroup, whatever the grid.  Waits are clock-bounded; once any wait has
-// expired (UBEP_ERR_TIMEOUT in the status word) later waits give up at once,
-// so a withheld row costs one time limit, not one per task.
+// expired (UBEP_ERR_TIMEOUT in the status word, and a give-up word in the
+// header whatever error the status word already holds) later waits give up
+// at once, so a withheld row costs one time limit, not one per task.  A
+// token whose own first eight channels hold the sentinel word can never look
+// arrived: its consumer reports UBEP_ERR_SENTINEL_DATA and does not wait.
 #include "launch.h"
 #include "rows.h"
 
@@ -103,24 +106,36 @@ __global__ __launch_bounds__(kSentBlock) void sentinel_kernel(SentArgs a) {
                                                              a.n_rows, gtid, status);
             wait_memory();             // every body unit of the block is at the coherent level
             __syncthreads();
-            if (has_t && gtid == 0 && (a.debug & 1u) == 0u) {
+            if ((a.debug & kDebugDelay) != 0u && blk % 3u == 0u) debug_delay();
+            if (has_t && gtid == 0 && (a.debug & kDebugWithhold) == 0u) {
                 const u32x4 head = a.x[t * a.nvec];
-                if (any_sentinel_word(head)) raise_status(status, UBEP_ERR_SENTINEL_DATA);
-                for (int32_t j = 0; j < a.k; ++j) {
-                    const int32_t q = a.pos[t * a.k + j];
-                    if (row_ok(q, a.n_rows))
-                        store16_device(row_rsrc(a.recv + (int64_t)q * a.nvec, a.nvec * 16), 0, head);
+                if (any_sentinel_word(head)) {
+                    // such a head could never signal arrival: leave the
+                    // sentinel in place (the consumer does not wait for it)
+                    raise_status(status, UBEP_ERR_SENTINEL_DATA);
+                } else {
+                    for (int32_t j = 0; j < a.k; ++j) {
+                        const int32_t q = a.pos[t * a.k + j];
+                        if (row_ok(q, a.n_rows))
+                            store16_device(row_rsrc(a.recv + (int64_t)q * a.nvec, a.nvec * 16), 0, head);
+                    }
                 }
             }
         } else {
             if (has_t && gtid == 0) {
+                // rows of a token whose own head holds the sentinel word never
+                // look arrived: report it (the producer does too) and skip the
+                // wait; only that token's output is then unspecified
+                const bool own_sentinel = any_sentinel_word(a.x[t * a.nvec]);
+                if (own_sentinel) raise_status(status, UBEP_ERR_SENTINEL_DATA);
                 const uint64_t t0 = now_ticks();
-                for (int32_t j = 0; j < a.k; ++j) {
+                for (int32_t j = 0; j < a.k && !own_sentinel; ++j) {
                     const int32_t q = a.pos[t * a.k + j];
                     if (!row_ok(q, a.n_rows)) continue;
                     const __amdgpu_buffer_rsrc_t rs = row_rsrc(a.recv + (int64_t)q * a.nvec, a.nvec * 16);
                     while (any_sentinel_word(poll16_device(rs))) {
-                        if (now_ticks() - t0 > a.spin_ticks || ld_relaxed(status) == UBEP_ERR_TIMEOUT) {
+                        if (now_ticks() - t0 > a.spin_ticks || ld_relaxed(&a.hdr[kHdrSentGiveUp]) != 0u) {
+                            st_relaxed(&a.hdr[kHdrSentGiveUp], 1u);
                             raise_status(status, UBEP_ERR_TIMEOUT);
                             break;
                         }
@@ -150,6 +165,7 @@ __global__ __launch_bounds__(kSentBlock) void sentinel_kernel(SentArgs a) {
         const uint32_t done = add_relaxed(&a.hdr[kHdrSentDone], 1u);
         if (done == gridDim.x - 1u) {
             st_relaxed(&a.hdr[kHdrSentTicket], 0u);
+            st_relaxed(&a.hdr[kHdrSentGiveUp], 0u);
             st_relaxed(&a.hdr[kHdrSentDone], 0u);
         }
     }

@@ -242,9 +242,13 @@ ubep_status ubep_combine(const ubep_shape *shape /*host*/, const void *y, const 
  * same bytes as ubep_dispatch(UBEP_BF16) followed by ubep_combine(y = recv),
  * for every chunk order.
  * spin_limit_ns bounds each flag wait (0 selects one second); an expired wait
- * sets UBEP_ERR_TIMEOUT, abandons that wait and lets the kernel finish.
+ * sets UBEP_ERR_TIMEOUT (unless the status word already holds an error),
+ * abandons that wait, makes every later wait of the call give up at once,
+ * and lets the kernel finish.
  * debug_flags must be 0 in normal use; bit 0 stops D tasks from raising flags
- * (used only to exercise the time-out path). */
+ * (used only to exercise the time-out path); bit 1 holds every third D task
+ * of a chunk back for about 25 us before it raises the flag (consumers then
+ * find their chunks late; results are unchanged). */
 ubep_status ubep_dispatch_combine_chunked(const ubep_shape *shape /*host*/, const void *x,
                                           const int32_t *pos, const float *topk_w, void *recv,
                                           void *out, const int32_t *chunk_order /*host*/,
@@ -266,13 +270,18 @@ ubep_status ubep_dispatch_combine_chunked(const ubep_shape *shape /*host*/, cons
  * hold the sentinel (ubep_recv_sentinel_init once after allocation; every
  * call leaves them so again, also after a time-out); no aligned pair of
  * channels among the first 8 of an x row is 0xFFFF 0xFFFF (reported as
- * UBEP_ERR_SENTINEL_DATA, and that token's wait then times out).
+ * UBEP_ERR_SENTINEL_DATA; that token's rows never signal arrival, so its
+ * consumer does not wait and its output is unspecified, while every other
+ * token is combined exactly).
  * Results: out is bit-identical to ubep_dispatch(UBEP_BF16) + ubep_combine
  * (y = recv); recv afterwards holds the dispatched rows except channels 0..7
  * of every row, which hold the sentinel.  spin_limit_ns bounds the waits
- * (0 selects one second); once one expires (UBEP_ERR_TIMEOUT) the rest give
- * up at once.  debug_flags must be 0 in normal use; bit 0 withholds every
- * row's channels 0..7 (only to exercise the time-out path). */
+ * (0 selects one second); once one expires (UBEP_ERR_TIMEOUT unless the
+ * status word already holds an error) the rest of the call's waits give up
+ * at once.  debug_flags must be 0 in normal use; bit 0 withholds every
+ * row's channels 0..7 (only to exercise the time-out path); bit 1 holds
+ * every third D task back for about 25 us before it writes the rows'
+ * channels 0..7 (consumers then find rows late; results are unchanged). */
 ubep_status ubep_dispatch_combine_sentinel(const ubep_shape *shape /*host*/, const void *x,
                                            const int32_t *pos, const float *topk_w, void *recv,
                                            void *out, uint64_t spin_limit_ns, uint32_t debug_flags,
@@ -297,8 +306,10 @@ ubep_status ubep_recv_sentinel_init(void *recv, int64_t rows, int64_t H, hipStre
  * expert_offset: int32 [E+1] device array, non-decreasing from 0 to at most
  * T*k (ubep_layout_grouped's output); rows outside every run are not written.
  * Limits: H % 64 == 0, H <= 2^22, N % 128 == 0, E <= 1024, ceil(T*k/128) + E <= 65535
- * (else UBEP_ERR_UNSUPPORTED).  An offset outside [0, T*k] sets
- * UBEP_ERR_BAD_POSITION and that expert's rows are skipped.  The workspace
+ * (else UBEP_ERR_UNSUPPORTED).  Offsets that are not non-decreasing from
+ * expert_offset[0] = 0 within [0, T*k] set UBEP_ERR_BAD_POSITION; an expert
+ * whose own run is reversed or reaches outside [0, T*k] is skipped (y is then
+ * unspecified).  The workspace
  * is used for the status word only.  One kernel on `stream`. */
 ubep_status ubep_expert_linear(const ubep_shape *shape /*host*/, int64_t N,
                                const int32_t *expert_offset, const void *x, const void *w,

@@ -80,3 +80,50 @@ def bf16_ordinal_distance(a: np.ndarray, b: np.ndarray) -> np.ndarray:
         u = u.astype(np.int64)
         return np.where(u & 0x8000, 0x8000 - (u & 0x7FFF), 0x8000 + u)
     return np.abs(ordv(a) - ordv(b))
+
+
+def token_slices(s, budget_bytes: int = 1 << 29):
+    """Contiguous token ranges whose k receive rows hold at most about
+    budget_bytes of bf16 (one range at least one token long)."""
+    step = max(1, budget_bytes // (s.k * s.H * 2))
+    return [(t0, min(s.T, t0 + step)) for t0 in range(0, s.T, step)]
+
+
+def assert_path_whole(b, w, skip_channels: int = 0, y=None):
+    """Every dispatched row and every combined token of the device buffers `b`
+    against the oracle, slice by slice: the oracle dispatches, applies the
+    identity expert to and combines each token range on its own (dispatch and
+    combine of a token touch only that token's k rows, so a range's results
+    equal the whole problem's there).  b.pos must already equal the oracle's
+    layout.  skip_channels: leading channels of every receive row not compared
+    (the sentinel pipeline leaves its readiness word there).  y: the device
+    combine input to compare as well (the fp8 identity expert's output)."""
+    s = w.shape
+    fp8 = w.recipe.payload == "fp8"
+    n_checked = 0
+    for t0, t1 in token_slices(s):
+        toks = np.arange(t0, t1)
+        rows_ref, out_ref = oracle.pipeline_tokens(w.x, w.topk_idx, w.topk_w, s.E, s.R, s.C,
+                                                   payload=w.recipe.payload, tokens=toks)
+        rows = b.pos[t0:t1].reshape(-1).long()
+        if fp8:
+            q_ref, sc_ref = rows_ref
+            q_ref = q_ref.reshape(-1, s.H)
+            sc_ref = sc_ref.reshape(-1, s.H // 128)
+            np.testing.assert_array_equal(to_np(b.recv.index_select(0, rows)), q_ref,
+                                          err_msg=f"fp8 codes, tokens {t0}..{t1}")
+            np.testing.assert_array_equal(to_np(b.recv_scale.index_select(0, rows)), sc_ref,
+                                          err_msg=f"fp8 scales, tokens {t0}..{t1}")
+            if y is not None:
+                np.testing.assert_array_equal(to_np(y.index_select(0, rows)),
+                                              oracle.identity_fp8(q_ref, sc_ref),
+                                              err_msg=f"identity expert, tokens {t0}..{t1}")
+        else:
+            got = to_np(b.recv.index_select(0, rows))
+            want = rows_ref.reshape(-1, s.H)
+            np.testing.assert_array_equal(got[:, skip_channels:], want[:, skip_channels:],
+                                          err_msg=f"dispatched rows, tokens {t0}..{t1}")
+        np.testing.assert_array_equal(to_np(b.out[t0:t1]), out_ref,
+                                      err_msg=f"combined tokens {t0}..{t1}")
+        n_checked += t1 - t0
+    assert n_checked == s.T

@@ -90,8 +90,10 @@ def test_validation_happens_before_any_launch():
     nws = L.ubep_workspace_bytes(C.byref(s2))
     assert L.ubep_dispatch_combine_chunked(C.byref(s2), 16, 16, 16, 16, 16, order, 0, 0, 256, nws,
                                            None) == ubep.ERR_INVALID_ARG
-    assert L.ubep_dispatch_combine_chunked(C.byref(s2), 16, 16, 16, 16, 16, None, 0, 2, 256, nws,
+    assert L.ubep_dispatch_combine_chunked(C.byref(s2), 16, 16, 16, 16, 16, None, 0, 4, 256, nws,
                                            None) == ubep.ERR_INVALID_ARG   # unknown debug flag
+    assert L.ubep_dispatch_combine_sentinel(C.byref(s2), 16, 16, 16, 16, 16, 0, 4, 256, nws,
+                                            None) == ubep.ERR_INVALID_ARG  # unknown debug flag
     assert ubep.status_str(ubep.ERR_TIMEOUT) == "ready-flag wait timed out"
 
 
@@ -143,7 +145,7 @@ def test_sentinel_pipeline_validation_without_gpu():
     nws = L.ubep_workspace_bytes(C.byref(s))
     assert L.ubep_dispatch_combine_sentinel(C.byref(s), 16, 16, 16, 16, None, 0, 0, 256, nws,
                                             None) == ubep.ERR_INVALID_ARG          # no out
-    assert L.ubep_dispatch_combine_sentinel(C.byref(s), 16, 16, 16, 16, 16, 0, 2, 256, nws,
+    assert L.ubep_dispatch_combine_sentinel(C.byref(s), 16, 16, 16, 16, 16, 0, 4, 256, nws,
                                             None) == ubep.ERR_INVALID_ARG          # unknown flag
     assert L.ubep_recv_sentinel_init(256, 4, 12, None) == ubep.ERR_INVALID_ARG   # H % 8 != 0
     assert L.ubep_recv_sentinel_init(8, 4, 16, None) == ubep.ERR_INVALID_ARG     # misaligned

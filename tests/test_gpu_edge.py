@@ -126,6 +126,61 @@ def test_chunked_timeout_is_reported_not_hung():
     np.testing.assert_array_equal(to_np(b.out), out)
 
 
+def test_chunked_late_producers_bit_exact():
+    """Debug bit 1 holds every third D task back (about 25 us) before it
+    raises its chunk's flag: C tasks wait on late chunks, results stay exact."""
+    w = custom(T=2048, H=1024, E=64, k=8, R=16, C=8, routing="zipf", seed=5)
+    s = w.shape
+    L = oracle.layout(w.topk_idx, s.E, s.R, s.C)
+    y = oracle.dispatch_bf16(w.x, L["pos"])
+    out = oracle.combine(y, L["pos"], w.topk_w)
+    b = upload(w)
+    sd = s.as_dict()
+    ubep.ubep_layout(sd, b.topk_idx, b.pos, b.expert_count, b.rank_count, b.recv_offset,
+                     b.send_offset, b.chunk_offset, b.recv_src, b.ws)
+    for call in range(2):
+        say(f"chunked late producers, call {call}")
+        b.out.zero_()
+        ubep.ubep_dispatch_combine_chunked(sd, b.x, b.pos, b.topk_w, b.recv, b.out, None, b.ws,
+                                           debug_flags=2)
+        torch.cuda.synchronize()
+        assert device_status(b) == ubep.OK
+        np.testing.assert_array_equal(to_np(b.recv), y)
+        np.testing.assert_array_equal(to_np(b.out), out)
+
+
+def test_chunked_gives_up_after_one_limit_whatever_the_status():
+    """A bad position is recorded first, then every flag is withheld: the
+    first expired wait must end all later ones (about one 50 ms limit, not
+    one per C task: 16384 of them on a few thousand workgroups)."""
+    import time
+    w = custom(T=65536, H=8, E=2, k=1, R=2, C=256, routing="topk", seed=6)
+    s = w.shape
+    sd = s.as_dict()
+    b = upload(w)
+    ubep.ubep_layout(sd, b.topk_idx, b.pos, b.expert_count, b.rank_count, b.recv_offset,
+                     b.send_offset, b.chunk_offset, b.recv_src, b.ws)
+    torch.cuda.synchronize()
+    pos0 = to_np(b.pos).copy()
+    pos = pos0.copy()
+    pos[0, 0] = s.T * s.k + 3
+    b.pos.copy_(torch.from_numpy(pos).cuda())
+    say("chunked give-up after a bad position (50 ms limit, flags withheld)")
+    t0 = time.perf_counter()
+    ubep.ubep_dispatch_combine_chunked(sd, b.x, b.pos, b.topk_w, b.recv, b.out, None, b.ws,
+                                       spin_limit_ns=50_000_000, debug_flags=1)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    assert device_status(b) == ubep.ERR_BAD_POSITION
+    assert dt < 0.3, f"{dt:.3f} s"
+    b.pos.copy_(torch.from_numpy(pos0).cuda())      # the give-up word was reset
+    run_path(b, chunked=True)
+    torch.cuda.synchronize()
+    assert device_status(b) == ubep.OK
+    out = oracle.combine(oracle.dispatch_bf16(w.x, pos0), pos0, w.topk_w)
+    np.testing.assert_array_equal(to_np(b.out), out)
+
+
 @pytest.mark.parametrize("order", ["identity", "reversed", "lpt", "random"])
 def test_chunked_order_invariance(order):
     w = custom(T=2048, H=1024, E=64, k=8, R=16, C=16, routing="zipf", seed=4)

@@ -207,3 +207,48 @@ def test_bad_expert_offsets_reported_and_skipped():
     e_of_row = np.repeat(np.arange(7), np.diff(good[:8]))
     _check_rows(xr[:lo], wb, e_of_row, _bits(y[:lo]), ref)
     assert not bool(y[lo:].view(torch.int16).any())  # expert 7's rows untouched
+
+
+@pytest.mark.parametrize("case", ["reversed", "nonzero_start"])
+def test_inconsistent_expert_offsets_reported(case):
+    """Offsets inside [0, T*k] that are not non-decreasing from 0 are reported.
+    reversed: expert 3's run ends before it starts, so it is skipped while the
+    runs that stay intact are computed as usual; nonzero_start: the offsets
+    start at 1, reported, and every run is still computed over its rows."""
+    w = custom(T=256, H=128, E=8, k=2, R=2, C=1, routing="topk", weights="softmax", seed=69)
+    s = w.shape
+    say(f"expert linear inconsistent offsets: {case}")
+    b = upload(w)
+    eoff = _grouped_layout(b)
+    ubep.ubep_dispatch(b.shape, ubep.BF16, b.x, b.pos, b.recv, None, b.ws)
+    torch.cuda.synchronize()
+    good = to_np(eoff).copy()
+    assert good[3] >= 2 and good[5] > good[4] > good[3]
+    bad = good.copy()
+    if case == "reversed":
+        bad[4] = good[3] - 1                        # run 3 = [good[3], good[3] - 1)
+    else:
+        bad[0] = 1
+    W = _weights(s.E, 128, s.H, 69, 0.05)
+    y = torch.zeros((s.T * s.k, 128), dtype=torch.bfloat16, device="cuda")
+    ubep.ubep_expert_linear(b.shape, 128, torch.from_numpy(bad).cuda(), b.recv, _packed(W), y, b.ws)
+    torch.cuda.synchronize()
+    assert device_status(b) == ubep.ERR_BAD_POSITION
+    xr, wb, yb = _bits(b.recv), _bits(W), _bits(y)
+    if case == "reversed":
+        keep = list(range(3)) + list(range(5, 8))   # experts whose runs are untouched
+    else:
+        keep = list(range(1, 8))
+    for e in keep:
+        lo, hi = int(good[e]), int(good[e + 1])
+        if e == 2 and case == "reversed":
+            hi -= 1                                  # its last row is also in expert 4's run
+        if hi <= lo:
+            continue
+        off = np.array([0, hi - lo], np.int32)
+        ref = oracle.expert_linear(xr[lo:hi], wb[e:e + 1], off)
+        _check_rows(xr[lo:hi], wb, np.full(hi - lo, e), yb[lo:hi], ref)
+    if case == "nonzero_start":                     # expert 0 over its rows from 1
+        lo, hi = 1, int(good[1])
+        ref = oracle.expert_linear(xr[lo:hi], wb[0:1], np.array([0, hi - lo], np.int32))
+        _check_rows(xr[lo:hi], wb, np.zeros(hi - lo, int), yb[lo:hi], ref)

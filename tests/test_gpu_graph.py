@@ -51,10 +51,17 @@ def test_graph_replays_match_eager(chunked):
 
 def test_graph_replays_decode_shape():
     w = make_config("dsv3_decode_T4096_H7168_E256_k8_R32")
+    s = w.shape
     b = upload(w)
     run_path(b)
     torch.cuda.synchronize()
+    # the eager result the replays must reproduce is itself the oracle's
+    L = oracle.layout(w.topk_idx, s.E, s.R, s.C)
     eager_out, eager_pos = to_np(b.out).copy(), to_np(b.pos).copy()
+    np.testing.assert_array_equal(eager_pos, L["pos"])
+    np.testing.assert_array_equal(eager_out,
+                                  oracle.combine(oracle.dispatch_bf16(w.x, L["pos"]), L["pos"],
+                                                 w.topk_w))
     other = upload(custom(T=128, H=1024, E=8, k=2, R=2, seed=43))
     say("graph replay decode shape")
     _replay_and_check(b, eager_out, eager_pos, False, other)

@@ -13,8 +13,9 @@ import combine_top_route_amd as ubep
 import oracle
 from combine_top_route_amd.buffers import alloc_buffers, run_path
 from workloads import CONFIGS, custom, generate
-from gpu_helpers import (assert_layout_equal, device_status, dtype_of, gpu_layout, oracle_layout,
-                         say, shape_of, to_np, upload, workload)
+from gpu_helpers import (LAYOUT_KEYS, assert_layout_equal, assert_path_whole, device_status,
+                         dtype_of, gpu_layout, oracle_layout, say, shape_of, to_np, upload,
+                         workload)
 
 pytestmark = pytest.mark.gpu
 
@@ -34,6 +35,13 @@ MEDIUM = [
     dict(T=4096, H=64, E=256, k=8, R=32, C=2, routing="topk", seed=5),      # several tiles
     dict(T=1000, H=64, E=10, k=10, R=5, C=1, routing="topk", seed=6),       # k = E
     dict(T=64, H=8, E=2, k=2, R=1, C=1, routing="topk", seed=7),            # one rank, tiny H
+    # the row kernels' instantiations that the full-size workloads run:
+    # H = 7168 (groups of 128 threads, 7 vectors each; decode and large
+    # prefill) with a ragged last block of one token, and H = 4096 (groups of
+    # 64 threads, 8 vectors each; the combine of the fp8 prefill)
+    dict(T=255, H=7168, E=40, k=8, R=5, C=3, routing="zipf", seed=10),
+    dict(T=512, H=7168, E=256, k=8, R=32, C=2, routing="topk", seed=11),
+    dict(T=384, H=4096, E=128, k=8, R=16, C=1, routing="topk", seed=12),
 ]
 
 
@@ -100,7 +108,13 @@ def test_layout_workers_taking_several_tiles(spec, cap, fused):
 
 
 @pytest.mark.parametrize("spec", [dict(T=256, H=512, E=16, k=4, R=4, C=2, routing="zipf", seed=8),
-                                  dict(T=128, H=1024, E=8, k=2, R=2, C=1, routing="topk", seed=9)])
+                                  dict(T=128, H=1024, E=8, k=2, R=2, C=1, routing="topk", seed=9),
+                                  # H = 4096: the 256-thread groups of the fp8 prefill
+                                  dict(T=384, H=4096, E=128, k=8, R=16, C=1, routing="topk", seed=13),
+                                  dict(T=129, H=4096, E=24, k=6, R=3, C=1, routing="zipf", seed=14),
+                                  # H = 7168 (56 blocks of 128 channels; 448 threads a row)
+                                  dict(T=64, H=7168, E=8, k=2, R=2, C=1, routing="topk", seed=15)],
+                         ids=lambda s: f"T{s['T']}H{s['H']}E{s['E']}k{s['k']}")
 def test_fp8_shapes_bit_exact(spec):
     _full_compare(_small_workload(spec, payload="fp8"))
 
@@ -115,7 +129,10 @@ def test_full_size_layout_bit_exact(name):
     assert_layout_equal(got, oracle_layout(w), w.shape.C)
 
 
-def _check_full_path(name, chunked=False, order=None, n_sample=48, fused=False):
+def _check_full_path(name, chunked=False, order=None, fused=False):
+    """The whole path at a full-size workload: layout bit-exact, then every
+    dispatched row (bf16 rows, or fp8 codes and scales and the identity
+    expert's output) and every combined token against the oracle."""
     w = workload(name)
     s = w.shape
     say(f"full path {name} chunked={chunked} order={order} fused={fused}")
@@ -123,54 +140,22 @@ def _check_full_path(name, chunked=False, order=None, n_sample=48, fused=False):
     run_path(b, chunked=chunked, chunk_order=order, fused=fused)
     torch.cuda.synchronize()
     assert device_status(b) == ubep.OK
-    L = oracle_layout(w)
-    np.testing.assert_array_equal(to_np(b.pos), L["pos"])
-    # every dispatched row, on the device: recv[pos[t][j]] == x[t]
-    pos_d = b.pos.to(torch.int64)
-    step = max(1, (1 << 28) // (s.k * s.H * 2))
-    for t0 in range(0, s.T, step):
-        t1 = min(s.T, t0 + step)
-        rows = pos_d[t0:t1].reshape(-1)
-        if b.dtype == ubep.BF16:
-            got = b.recv.index_select(0, rows).view(t1 - t0, s.k, s.H)
-            want = b.x[t0:t1].unsqueeze(1).expand(-1, s.k, -1)
-            assert torch.equal(got.view(torch.int16), want.view(torch.int16)), (t0, t1)
-        else:   # every slot of a token carries the same codes and scales
-            got = b.recv.index_select(0, rows).view(t1 - t0, s.k, s.H)
-            assert torch.equal(got, got[:, :1].expand(-1, s.k, -1)), (t0, t1)
-            gs = b.recv_scale.index_select(0, rows).view(t1 - t0, s.k, -1)
-            assert torch.equal(gs, gs[:, :1].expand(-1, s.k, -1)), (t0, t1)
-    # sampled tokens against the oracle's own dispatch -> identity -> combine
-    rng = np.random.default_rng(0)
-    toks = np.unique(np.concatenate([[0, s.T - 1], rng.integers(0, s.T, n_sample)]))
-    rows_ref, out_ref = oracle.pipeline_tokens(w.x, w.topk_idx, w.topk_w, s.E, s.R, s.C,
-                                               payload=w.recipe.payload, tokens=toks)
-    pos_t = L["pos"][toks]
-    if w.recipe.payload == "fp8":
-        q_ref, s_ref = rows_ref
-        np.testing.assert_array_equal(to_np(b.recv[torch.from_numpy(pos_t.ravel()).cuda().long()]),
-                                      q_ref.reshape(-1, s.H))
-        np.testing.assert_array_equal(
-            to_np(b.recv_scale[torch.from_numpy(pos_t.ravel()).cuda().long()]),
-            s_ref.reshape(-1, s.H // 128))
-    else:
-        np.testing.assert_array_equal(to_np(b.recv[torch.from_numpy(pos_t.ravel()).cuda().long()]),
-                                      rows_ref.reshape(-1, s.H))
-    np.testing.assert_array_equal(to_np(b.out[torch.from_numpy(toks).cuda()]), out_ref)
+    assert_layout_equal({k: to_np(getattr(b, k)) for k in LAYOUT_KEYS}, oracle_layout(w), s.C)
+    assert_path_whole(b, w, y=b.y if w.recipe.payload == "fp8" else None)
     return b
 
 
-@pytest.mark.parametrize("name", FULL[:3])
-def test_full_size_path_sampled(name):
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_path_whole_output(name):
     _check_full_path(name)
 
 
 @pytest.mark.parametrize("name", FULL[:2])
-def test_full_size_fused_layout_dispatch_sampled(name):
+def test_full_size_fused_layout_dispatch_whole_output(name):
     _check_full_path(name, fused=True)
 
 
-def test_large_prefill_chunked_sampled():
+def test_large_prefill_chunked_whole_output():
     _check_full_path("prefill_grouped_zipf_T65536_H7168_E256_k8_R64_C16", chunked=True)
 
 

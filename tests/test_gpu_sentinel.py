@@ -11,7 +11,7 @@ import combine_top_route_amd as ubep
 import oracle
 from combine_top_route_amd.buffers import run_path
 from workloads import custom
-from gpu_helpers import device_status, say, to_np, upload, workload
+from gpu_helpers import assert_path_whole, device_status, say, to_np, upload, workload
 
 pytestmark = pytest.mark.gpu
 
@@ -67,28 +67,24 @@ def test_sentinel_pipeline_bit_exact(spec):
 @pytest.mark.parametrize("name", ["dsv3_decode_T4096_H7168_E256_k8_R32",
                                   "dsv3_decode_zipf_T4096_H7168_E256_k8_R32"])
 def test_sentinel_pipeline_full_size(name):
+    """Full-size decode workloads: every combined token and every dispatched
+    row (past the sentinel channels) against the oracle, on two calls in a row."""
     w = workload(name)
     s = w.shape
     say(f"sentinel pipeline full size {name}")
     b = upload(w)
-    run_path(b)                                    # unfused reference on the device
-    torch.cuda.synchronize()
-    ref_out = b.out.clone()
     ubep.ubep_recv_sentinel_init(b.recv, s.T * s.k, s.H)
-    b.out.zero_()
-    _run(b)
-    assert device_status(b) == ubep.OK
-    assert torch.equal(b.out.view(torch.int16), ref_out.view(torch.int16))
-    head = b.recv[:, :8].contiguous().view(torch.int16)
-    assert bool((head == -1).all())
-    # every dispatched row past channel 7: recv[pos[t][j], 8:] == x[t, 8:]
-    got = b.recv.index_select(0, b.pos.reshape(-1).long()).view(s.T, s.k, s.H)[:, :, 8:]
-    want = b.x[:, 8:].unsqueeze(1).expand(-1, s.k, -1)
-    assert torch.equal(got.view(torch.int16), want.view(torch.int16))
-    rng = np.random.default_rng(5)
-    toks = np.unique(np.concatenate([[0, s.T - 1], rng.integers(0, s.T, 48)]))
-    _, out_ref = oracle.pipeline_tokens(w.x, w.topk_idx, w.topk_w, s.E, s.R, tokens=toks)
-    np.testing.assert_array_equal(to_np(b.out[torch.from_numpy(toks).cuda()]), out_ref)
+    _layout(b)
+    torch.cuda.synchronize()
+    L = oracle.layout(w.topk_idx, s.E, s.R, s.C)
+    np.testing.assert_array_equal(to_np(b.pos), L["pos"])
+    for call in range(2):          # the second call relies on the restored sentinels
+        b.out.zero_()
+        _run(b)
+        assert device_status(b) == ubep.OK, call
+        head = b.recv[:, :8].contiguous().view(torch.int16)
+        assert bool((head == -1).all())
+        assert_path_whole(b, w, skip_channels=8)
 
 
 def test_sentinel_timeout_is_reported_not_hung():
@@ -147,3 +143,54 @@ def test_sentinel_bad_position_skipped():
     wts = w.topk_w.copy()
     wts[20, 1] = 0.0
     np.testing.assert_array_equal(to_np(b.out), oracle.combine(y, pos0, wts))
+
+
+def test_sentinel_late_producers_bit_exact():
+    """Debug bit 1 holds every third producer back (about 25 us) before it
+    writes the rows' first channels: consumers meet rows that arrive late,
+    and the results stay exact on two calls in a row."""
+    w = custom(T=2048, H=1024, E=64, k=8, R=8, C=1, routing="zipf", weights="softmax", seed=61)
+    s = w.shape
+    b = upload(w)
+    ubep.ubep_recv_sentinel_init(b.recv, s.T * s.k, s.H)
+    _layout(b)
+    L = oracle.layout(w.topk_idx, s.E, s.R, s.C)
+    recv = oracle.dispatch_bf16(w.x, L["pos"])
+    out = oracle.combine(recv, L["pos"], w.topk_w)
+    for call in range(2):
+        say(f"sentinel late producers, call {call}")
+        b.out.zero_()
+        _run(b, debug_flags=2)
+        assert device_status(b) == ubep.OK, call
+        np.testing.assert_array_equal(to_np(b.out), out)
+        _check_recv(b.recv, recv)
+
+
+def test_sentinel_gives_up_after_one_limit_whatever_the_status():
+    """A bad position is recorded first, then every row head is withheld: the
+    first expired wait must end all later ones although the status word
+    keeps the earlier error (about one 50 ms limit in all, not one per task:
+    16384 tasks on a few thousand workgroups)."""
+    import time
+    w = custom(T=65536, H=8, E=2, k=1, R=2, C=1, routing="topk", weights="softmax", seed=62)
+    s = w.shape
+    b = upload(w)
+    ubep.ubep_recv_sentinel_init(b.recv, s.T * s.k, s.H)
+    _layout(b)
+    torch.cuda.synchronize()
+    pos0 = to_np(b.pos).copy()
+    pos = pos0.copy()
+    pos[0, 0] = s.T * s.k + 3
+    b.pos.copy_(torch.from_numpy(pos).cuda())
+    say("sentinel give-up after a bad position (50 ms limit, heads withheld)")
+    t0 = time.perf_counter()
+    _run(b, spin_limit_ns=50_000_000, debug_flags=1)
+    dt = time.perf_counter() - t0
+    assert device_status(b) == ubep.ERR_BAD_POSITION
+    assert dt < 0.3, f"{dt:.3f} s"
+    assert np.all(to_np(b.recv)[:, :8] == SENT)
+    b.pos.copy_(torch.from_numpy(pos0).cuda())      # the give-up word was reset
+    _run(b)
+    assert device_status(b) == ubep.OK
+    out = oracle.combine(oracle.dispatch_bf16(w.x, pos0), pos0, w.topk_w)
+    np.testing.assert_array_equal(to_np(b.out), out)
