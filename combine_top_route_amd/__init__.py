@@ -11,7 +11,8 @@ from ._abi import (BF16, ERR_BAD_EXPERT_ID, ERR_BAD_POSITION, ERR_HIP, ERR_INVAL
                    ubep_dispatch_combine_chunked, ubep_dispatch_combine_sentinel, ubep_expert_linear,
                    ubep_expert_pack_weights,
                    ubep_get_device_status, ubep_recv_sentinel_init, ubep_identity_expert_fp8,
-                   ubep_layout, ubep_layout_dispatch, ubep_layout_grouped, ubep_set_layout_workers,
+                   ubep_layout, ubep_layout_dispatch, ubep_layout_grouped, ubep_layout_noalloc,
+                   ubep_set_layout_workers,
                    ubep_shape,
                    ubep_time_next_launch, ubep_workspace_bytes, ubep_workspace_init)
 from .buffers import Buffers, alloc_buffers

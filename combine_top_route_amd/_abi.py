@@ -71,6 +71,7 @@ def lib() -> C.CDLL:
             "ubep_workspace_bytes": ([S], SZ),
             "ubep_workspace_init": ([P, SZ, P], C.c_int),
             "ubep_layout": ([S, P, P, P, P, P, P, P, P, P, SZ, P], C.c_int),
+            "ubep_layout_noalloc": ([S, P, P, P, P, P, P, P, P, P, C.c_int, P], C.c_int),
             "ubep_layout_grouped": ([S, P, P, P, P, P, P, P, P, P, P, SZ, P], C.c_int),
             "ubep_gate": ([C.POINTER(ubep_gate_shape), P, P, P, P], C.c_int),
             "ubep_layout_dispatch": ([S, P, P, P, P, P, P, P, P, P, P, P, SZ, P], C.c_int),
@@ -165,6 +166,15 @@ def ubep_layout(shape, topk_idx, pos, expert_count, rank_count, recv_offset, sen
                              _ptr(rank_count), _ptr(recv_offset), _ptr(send_offset),
                              _ptr(chunk_offset), _ptr(recv_src), _ptr(ws), _nbytes(ws),
                              _stream(stream)), "ubep_layout")
+
+
+def ubep_layout_noalloc(shape, topk_idx, pos, expert_count, rank_count, recv_offset, send_offset,
+                        chunk_offset, recv_src, status, reset=0, stream=None):
+    s = _shape(shape)
+    _check(lib().ubep_layout_noalloc(C.byref(s), _ptr(topk_idx), _ptr(pos), _ptr(expert_count),
+                                     _ptr(rank_count), _ptr(recv_offset), _ptr(send_offset),
+                                     _ptr(chunk_offset), _ptr(recv_src), _ptr(status), int(reset),
+                                     _stream(stream)), "ubep_layout_noalloc")
 
 
 def ubep_layout_grouped(shape, topk_idx, pos, expert_count, expert_offset, rank_count, recv_offset,

@@ -176,6 +176,36 @@ ubep_status ubep_layout(const ubep_shape* s, const int32_t* topk_idx, int32_t* p
                                     stream));
 }
 
+ubep_status ubep_layout_noalloc(const ubep_shape* s, const int32_t* topk_idx, int32_t* pos,
+                                int32_t* expert_count, int32_t* rank_count, int32_t* recv_offset,
+                                int32_t* send_offset, int32_t* chunk_offset, int32_t* recv_src,
+                                uint32_t* status, int reset, hipStream_t stream) {
+    Plan p;
+    const ubep_status st = check_and_plan(s, UBEP_BF16, &p);
+    if (st != UBEP_OK) return st;
+    if (!topk_idx || !pos || !expert_count || !rank_count || !recv_offset || !send_offset || !status)
+        return UBEP_ERR_INVALID_ARG;
+    if (!aligned(status, 4)) return UBEP_ERR_INVALID_ARG;
+    if (p.ws_bytes > kScratchBytes) return UBEP_ERR_UNSUPPORTED;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return UBEP_ERR_HIP;
+    void* ws = nullptr;
+    bool first_use = false;
+    if (layout_scratch(dev, &ws, &first_use) != hipSuccess) return UBEP_ERR_HIP;
+    uint64_t ticks;
+    const ubep_status ts = spin_ticks_for(0, &ticks);
+    if (ts != UBEP_OK) return ts;
+    // the array starts cleared on its first use on this device, and again
+    // whenever the caller asks (after a call that reported a time-out)
+    if (first_use || reset != 0) {
+        const hipError_t e = launch_fill_zero(ws, first_use ? kScratchBytes : p.ws_bytes, stream);
+        if (e != hipSuccess) return UBEP_ERR_HIP;
+    }
+    return hip_status(launch_layout(p, topk_idx, pos, expert_count, nullptr, rank_count,
+                                    recv_offset, send_offset, chunk_offset, recv_src, ws, ticks,
+                                    stream, status));
+}
+
 ubep_status ubep_layout_grouped(const ubep_shape* s, const int32_t* topk_idx, int32_t* pos,
                                 int32_t* expert_count, int32_t* expert_offset, int32_t* rank_count,
                                 int32_t* recv_offset, int32_t* send_offset, int32_t* chunk_offset,

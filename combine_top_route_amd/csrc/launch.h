@@ -40,10 +40,16 @@ hipError_t launch_kernel(void (*kernel)(P...), dim3 grid, dim3 block, size_t lds
 }
 
 // expert_offset: [E+1] output of the expert order (p.order == 1), may be null.
+// status: the device status word (null: the one in the workspace header).
 hipError_t launch_layout(const Plan& p, const int32_t* idx, int32_t* pos, int32_t* expert_count,
                          int32_t* expert_offset, int32_t* rank_count, int32_t* recv_offset,
                          int32_t* send_offset, int32_t* chunk_offset, int32_t* recv_src, void* ws,
-                         uint64_t spin_ticks, hipStream_t stream);
+                         uint64_t spin_ticks, hipStream_t stream, uint32_t* status = nullptr);
+
+// Device address of the allocation-free layout's per-device scratch array
+// (kScratchBytes), found once per device with that device current;
+// *first_use is true on the call that found it.
+hipError_t layout_scratch(int device, void** out, bool* first_use);
 
 int64_t layout_workers(const Plan& p, int cus);
 bool layout_lds_fits(const Plan& p);

@@ -13,6 +13,7 @@
 // trips (ticket, publish, look-back, totals) that bound the persistent
 // kernel's latency.
 #include <atomic>
+#include <mutex>
 
 #include "launch.h"
 #include "layout_worker.h"
@@ -195,8 +196,8 @@ __global__ __launch_bounds__(kSingleThreads) void layout_single_kernel(LayoutArg
             }
         }
     }
-    if (bad) raise_status(&a.hdr[kHdrStatus], UBEP_ERR_BAD_EXPERT_ID);
-    if (bad_pos) raise_status(&a.hdr[kHdrStatus], UBEP_ERR_BAD_POSITION);
+    if (bad) raise_status(a.status, UBEP_ERR_BAD_EXPERT_ID);
+    if (bad_pos) raise_status(a.status, UBEP_ERR_BAD_POSITION);
 }
 
 // LDS of the persistent layout's workgroup within what a CU offers (the
@@ -223,10 +224,35 @@ int64_t layout_workers(const Plan& p, int cus) {
     return n;
 }
 
+// ---------------------------------------------------------------- allocation-free layout
+// The workspace of ubep_layout_noalloc: one array per device for the life of
+// the process, shared by every such call on that device.  Host code never
+// uses its name as an address (on the host it names a stand-in): the device
+// address comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+hipError_t layout_scratch(int device, void** out, bool* first_use) {
+    static std::mutex mu;
+    static void* ptr[kScratchMaxDevices] = {};
+    if (device < 0 || device >= kScratchMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    *first_use = false;
+    if (ptr[device] == nullptr) {
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (p == nullptr) return hipErrorInvalidSymbol;
+        ptr[device] = p;
+        *first_use = true;
+    }
+    *out = ptr[device];
+    return hipSuccess;
+}
+
 hipError_t launch_layout(const Plan& p, const int32_t* idx, int32_t* pos, int32_t* expert_count,
                          int32_t* expert_offset, int32_t* rank_count, int32_t* recv_offset,
                          int32_t* send_offset, int32_t* chunk_offset, int32_t* recv_src, void* ws,
-                         uint64_t spin_ticks, hipStream_t stream) {
+                         uint64_t spin_ticks, hipStream_t stream, uint32_t* status) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
@@ -250,6 +276,7 @@ hipError_t launch_layout(const Plan& p, const int32_t* idx, int32_t* pos, int32_
     a.wbase = reinterpret_cast<int32_t*>(base + p.off_wbase);
     a.p = p;
     a.spin_ticks = spin_ticks;
+    a.status = status != nullptr ? status : a.hdr + kHdrStatus;
     if (layout_fits_one_group(p)) {
         const int64_t tpw = (p.n_tiles + kSingleWaves - 1) / kSingleWaves;
         const int64_t steps = tpw * p.tile_rows / 64;

@@ -160,6 +160,7 @@ hipError_t launch_layout_dispatch(const Plan& p, const int32_t* idx, const void*
     a.wbase = reinterpret_cast<int32_t*>(base + p.off_wbase);
     a.p = p;
     a.spin_ticks = spin_ticks;
+    a.status = status;
     const uint32_t n_workers = (uint32_t)layout_workers(p, di.cus);
     const unsigned lds = (unsigned)layout_lds_bytes(p, kFusedWaves);
     int G, VPT;

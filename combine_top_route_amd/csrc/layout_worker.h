@@ -62,6 +62,7 @@ struct LayoutArgs {
     Plan p;
     uint64_t spin_ticks;
     int32_t* expert_offset;  // [E+1], expert order only (may be null)
+    uint32_t* status;        // device status word (first error wins)
 };
 
 // LDS of one worker, carved from the kernel's dynamic shared memory.
@@ -582,9 +583,9 @@ __device__ __forceinline__ void layout_worker(const LayoutArgs& a, const LayoutL
         }
     }
 
-    if (bad) raise_status(&a.hdr[kHdrStatus], UBEP_ERR_BAD_EXPERT_ID);
-    if (timed_out) raise_status(&a.hdr[kHdrStatus], UBEP_ERR_TIMEOUT);
-    if (bad_pos) raise_status(&a.hdr[kHdrStatus], UBEP_ERR_BAD_POSITION);
+    if (bad) raise_status(a.status, UBEP_ERR_BAD_EXPERT_ID);
+    if (timed_out) raise_status(a.status, UBEP_ERR_TIMEOUT);
+    if (bad_pos) raise_status(a.status, UBEP_ERR_BAD_POSITION);
 }
 
 // Reset the tickets and counters and advance the epoch (done by the last

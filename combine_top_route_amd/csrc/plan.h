@@ -63,6 +63,10 @@ constexpr int64_t kGatherMaxTiles = 512;
 constexpr int kGatherMaxMine = 8;
 constexpr int kGatherBurst = 8;                  // state words a thread loads at once
 constexpr int64_t kMaxStateWords = (int64_t)1 << 26;                   // look-back state cap
+// Per-device scratch array of the allocation-free layout (ubep_layout_noalloc):
+// the largest workspace it serves.
+constexpr size_t kScratchBytes = (size_t)8 << 20;
+constexpr int kScratchMaxDevices = 64;
 
 struct Plan {
     int64_t T, H;

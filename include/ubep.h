@@ -132,6 +132,27 @@ ubep_status ubep_layout(const ubep_shape *shape /*host*/, const int32_t *topk_id
                         int32_t *recv_offset, int32_t *send_offset, int32_t *chunk_offset,
                         int32_t *recv_src, void *ws, size_t ws_bytes, hipStream_t stream);
 
+/* ubep_layout for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, hosts that forbid allocation): the same
+ * outputs, bit for bit, with no workspace argument.  Its workspace is one
+ * static device array of 8 MiB per GPU that the library holds until the
+ * process ends; every ubep_layout_noalloc call on that GPU shares it, and it
+ * keeps the last call's contents.  Calls that overlap on one GPU (on
+ * different streams, or from several host threads without ordering) race on
+ * it and give undefined results: order them on one stream.  The call itself
+ * allocates nothing (no hipMalloc / hipFree, no allocating library routine);
+ * the first call on a device looks the array up and clears it with a fill
+ * kernel on `stream`, and a nonzero `reset` clears the part this shape uses
+ * again first (pass it after a call that reported UBEP_ERR_TIMEOUT).
+ * status: caller-owned device uint32 that a detected error sets from 0 to its
+ * ubep_status code (first error wins, as the workspace status word; the call
+ * never clears it).  A shape whose ubep_workspace_bytes exceeds 8 MiB returns
+ * UBEP_ERR_UNSUPPORTED before anything is enqueued. */
+ubep_status ubep_layout_noalloc(const ubep_shape *shape /*host*/, const int32_t *topk_idx,
+                                int32_t *pos, int32_t *expert_count, int32_t *rank_count,
+                                int32_t *recv_offset, int32_t *send_offset, int32_t *chunk_offset,
+                                int32_t *recv_src, uint32_t *status, int reset, hipStream_t stream);
+
 /* Expert-grouped layout: the same call as ubep_layout, except that inside
  * each rank's region the rows are ordered by (expert, token, slot), so every
  * expert's rows form one contiguous run -- the order a grouped per-expert
