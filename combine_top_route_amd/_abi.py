@@ -1,4 +1,4 @@
-"""ctypes binding of libubep.so (include/ubep.h).
+"""ctypes binding of libubep.so (include/ubep.h, include/ubep_testing.h).
 
 Argument marshalling only: tensors become raw pointers, the current torch
 stream becomes the HIP stream, and a non-zero ubep_status raises UbepError.
@@ -77,7 +77,8 @@ def lib() -> C.CDLL:
             "ubep_layout_dispatch": ([S, P, P, P, P, P, P, P, P, P, P, P, SZ, P], C.c_int),
             "ubep_dispatch": ([S, C.c_int, P, P, P, P, P, SZ, P], C.c_int),
             "ubep_combine": ([S, P, P, P, P, P, SZ, P], C.c_int),
-            "ubep_dispatch_combine_chunked": ([S, P, P, P, P, P, P, U64, U32, P, SZ, P], C.c_int),
+            "ubep_dispatch_combine_chunked": ([S, P, P, P, P, P, P, P, P, U64, U32, P, SZ, P], C.c_int),
+            "ubep_chunk_order_lpt": ([S, P, P, P, P], C.c_int),
             "ubep_dispatch_combine_sentinel": ([S, P, P, P, P, P, U64, U32, P, SZ, P], C.c_int),
             "ubep_recv_sentinel_init": ([P, I64, I64, P], C.c_int),
             "ubep_expert_linear": ([S, I64, P, P, P, P, P, SZ, P], C.c_int),
@@ -85,6 +86,7 @@ def lib() -> C.CDLL:
             "ubep_get_device_status": ([P, SZ, P, C.POINTER(C.c_int)], C.c_int),
             "ubep_identity_expert_fp8": ([I64, I64, P, P, P, P], C.c_int),
             "ubep_copy": ([P, P, SZ, P], C.c_int),
+            "ubep_stream_probe": ([P, P, I64, C.c_int, C.c_int, P], C.c_int),
             "ubep_set_layout_workers": ([I32], C.c_int),
             "ubep_time_next_launch": ([P, P], C.c_int),
         }
@@ -209,15 +211,25 @@ def ubep_combine(shape, y, pos, topk_w, out, ws, stream=None):
 
 
 def ubep_dispatch_combine_chunked(shape, x, pos, topk_w, recv, out, chunk_order, ws,
-                                  spin_limit_ns: int = 0, debug_flags: int = 0, stream=None):
+                                  spin_limit_ns: int = 0, debug_flags: int = 0, stream=None,
+                                  chunk_offset=None, rank_count=None):
+    """chunk_order: a host sequence of chunk ids, or None; chunk_offset and
+    rank_count (device tensors from ubep_layout): the LPT order on the device."""
     s = _shape(shape)
     order = None
     if chunk_order is not None:
         order = (C.c_int32 * len(chunk_order))(*[int(c) for c in chunk_order])
     _check(lib().ubep_dispatch_combine_chunked(
         C.byref(s), _ptr(x), _ptr(pos), _ptr(topk_w), _ptr(recv), _ptr(out),
-        C.cast(order, C.c_void_p) if order is not None else None, spin_limit_ns, debug_flags,
-        _ptr(ws), _nbytes(ws), _stream(stream)), "ubep_dispatch_combine_chunked")
+        C.cast(order, C.c_void_p) if order is not None else None, _ptr(chunk_offset),
+        _ptr(rank_count), spin_limit_ns, debug_flags, _ptr(ws), _nbytes(ws), _stream(stream)),
+        "ubep_dispatch_combine_chunked")
+
+
+def ubep_chunk_order_lpt(shape, chunk_offset, rank_count, order, stream=None):
+    s = _shape(shape)
+    _check(lib().ubep_chunk_order_lpt(C.byref(s), _ptr(chunk_offset), _ptr(rank_count), _ptr(order),
+                                      _stream(stream)), "ubep_chunk_order_lpt")
 
 
 def ubep_dispatch_combine_sentinel(shape, x, pos, topk_w, recv, out, ws, spin_limit_ns: int = 0,
@@ -259,6 +271,11 @@ def ubep_identity_expert_fp8(rows, H, q, scale, y, stream=None):
 
 def ubep_copy(src, dst, nbytes, stream=None):
     _check(lib().ubep_copy(_ptr(src), _ptr(dst), nbytes, _stream(stream)), "ubep_copy")
+
+
+def ubep_stream_probe(src, dst, n_vec, fan_in, fan_out, stream=None):
+    _check(lib().ubep_stream_probe(_ptr(src), _ptr(dst), int(n_vec), int(fan_in), int(fan_out),
+                                   _stream(stream)), "ubep_stream_probe")
 
 
 def ubep_time_next_launch(start, stop):

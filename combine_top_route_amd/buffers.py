@@ -77,7 +77,9 @@ def alloc_buffers(shape: dict, dtype: int = _abi.BF16, device="cuda", x_bits=Non
 
 def run_path(b: Buffers, stream=None, chunked: bool = False, chunk_order=None, fused: bool = False):
     """Layout, dispatch, identity expert, combine on the buffers (library calls).
-    fused: layout and dispatch in one launch (bf16 payload, not chunked)."""
+    fused: layout and dispatch in one launch (bf16 payload, not chunked).
+    chunk_order (chunked): a host list of chunk ids, None (index order), or
+    "lpt" (the imbalance-aware order computed on the device)."""
     s = b.shape
     if fused and not chunked and b.dtype == _abi.BF16:
         _abi.ubep_layout_dispatch(s, b.topk_idx, b.x, b.pos, b.expert_count, b.rank_count,
@@ -90,8 +92,14 @@ def run_path(b: Buffers, stream=None, chunked: bool = False, chunk_order=None, f
                      b.send_offset, b.chunk_offset if s["C"] > 1 else None, b.recv_src, b.ws,
                      stream)
     if chunked:
-        _abi.ubep_dispatch_combine_chunked(s, b.x, b.pos, b.topk_w, b.recv, b.out, chunk_order,
-                                           b.ws, stream=stream)
+        if isinstance(chunk_order, str) and chunk_order == "lpt":   # the device's LPT order
+            _abi.ubep_dispatch_combine_chunked(s, b.x, b.pos, b.topk_w, b.recv, b.out, None, b.ws,
+                                               stream=stream,
+                                               chunk_offset=b.chunk_offset if s["C"] > 1 else None,
+                                               rank_count=b.rank_count)
+        else:
+            _abi.ubep_dispatch_combine_chunked(s, b.x, b.pos, b.topk_w, b.recv, b.out, chunk_order,
+                                               b.ws, stream=stream)
         return
     _abi.ubep_dispatch(s, b.dtype, b.x, b.pos, b.recv, b.recv_scale, b.ws, stream)
     if b.dtype == _abi.FP8_E4M3:

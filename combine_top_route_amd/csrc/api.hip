@@ -4,6 +4,7 @@
 
 #include "launch.h"
 #include "ubep.h"
+#include "ubep_testing.h"
 
 namespace ubep {
 
@@ -74,6 +75,8 @@ void make_plan(const ubep_shape& s, Plan* p, int order) {
     off = align_up(off + (size_t)p->n_tiles * kLayoutWaves * s.E * 4, 256);
     p->off_flags = off;
     off = align_up(off + (size_t)s.C * kFlagStride * 4, 256);
+    p->off_order = off;
+    off = align_up(off + (size_t)s.C * 4, 256);
     p->ws_bytes = off;
 }
 
@@ -291,15 +294,34 @@ ubep_status ubep_combine(const ubep_shape* s, const void* y, const int32_t* pos,
     return hip_status(launch_combine(p, y, pos, topk_w, out, status, stream));
 }
 
+ubep_status ubep_chunk_order_lpt(const ubep_shape* s, const int32_t* chunk_offset,
+                                 const int32_t* rank_count, int32_t* order, hipStream_t stream) {
+    Plan p;
+    const ubep_status st = check_and_plan(s, UBEP_BF16, &p);
+    if (st != UBEP_OK) return st;
+    if (!rank_count || !order || (p.C > 1 && !chunk_offset)) return UBEP_ERR_INVALID_ARG;
+    if (!aligned(rank_count, 4) || !aligned(order, 4) || (chunk_offset && !aligned(chunk_offset, 4)))
+        return UBEP_ERR_INVALID_ARG;
+    return hip_status(launch_chunk_lpt(p, chunk_offset, rank_count, order, stream));
+}
+
 ubep_status ubep_dispatch_combine_chunked(const ubep_shape* s, const void* x, const int32_t* pos,
                                           const float* topk_w, void* recv, void* out,
-                                          const int32_t* chunk_order, uint64_t spin_limit_ns,
+                                          const int32_t* chunk_order, const int32_t* chunk_offset,
+                                          const int32_t* rank_count, uint64_t spin_limit_ns,
                                           uint32_t debug_flags, void* ws, size_t ws_bytes,
                                           hipStream_t stream) {
     Plan p;
     const ubep_status st = check_and_plan(s, UBEP_BF16, &p);
     if (st != UBEP_OK) return st;
     if (!x || !pos || !topk_w || !recv || !out || !ws) return UBEP_ERR_INVALID_ARG;
+    // LPT policy: both layout outputs given (chunk_offset may be null for C = 1), no host order
+    const bool lpt = rank_count != nullptr;
+    if (lpt && (chunk_order != nullptr || (p.C > 1 && chunk_offset == nullptr)))
+        return UBEP_ERR_INVALID_ARG;
+    if (!lpt && chunk_offset != nullptr) return UBEP_ERR_INVALID_ARG;
+    if (lpt && (!aligned(rank_count, 4) || (chunk_offset && !aligned(chunk_offset, 4))))
+        return UBEP_ERR_INVALID_ARG;
     if (ws_bytes < p.ws_bytes || !aligned(ws, 256)) return UBEP_ERR_INVALID_ARG;
     if (!aligned(x, 16) || !aligned(recv, 16) || !aligned(out, 16)) return UBEP_ERR_INVALID_ARG;
     if (debug_flags & ~3u) return UBEP_ERR_INVALID_ARG;
@@ -316,8 +338,17 @@ ubep_status ubep_dispatch_combine_chunked(const ubep_shape* s, const void* x, co
     if (ts != UBEP_OK) return ts;
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return UBEP_ERR_HIP;
-    return hip_status(launch_chunked(p, x, pos, topk_w, recv, out, chunk_order, ticks, debug_flags,
-                                     ws, dev, stream));
+    int32_t* dev_order = nullptr;
+    if (lpt) {
+        // the order kernel leaves a pending timing pair to the pipeline kernel
+        const LaunchEvents ev = take_launch_events();
+        dev_order = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + p.off_order);
+        const hipError_t e = launch_chunk_lpt(p, chunk_offset, rank_count, dev_order, stream);
+        set_launch_events(ev.start, ev.stop);
+        if (e != hipSuccess) return UBEP_ERR_HIP;
+    }
+    return hip_status(launch_chunked(p, x, pos, topk_w, recv, out, chunk_order, dev_order, ticks,
+                                     debug_flags, ws, dev, stream));
 }
 
 ubep_status ubep_dispatch_combine_sentinel(const ubep_shape* s, const void* x, const int32_t* pos,
@@ -402,6 +433,17 @@ ubep_status ubep_copy(const void* src, void* dst, size_t bytes, hipStream_t stre
         return UBEP_ERR_INVALID_ARG;
     if (bytes == 0) return UBEP_OK;
     return hip_status(launch_copy(src, dst, bytes, stream));
+}
+
+ubep_status ubep_stream_probe(const void* src, void* dst, int64_t n_vec, int fan_in, int fan_out,
+                              hipStream_t stream) {
+    const bool shape_ok = (fan_in == 0 || fan_in == 1 || fan_in == 8) &&
+                          (fan_out == 0 || fan_out == 1 || fan_out == 8) && fan_in + fan_out > 0;
+    if (!shape_ok || n_vec < 0 || !dst || (fan_in > 0 && !src)) return UBEP_ERR_INVALID_ARG;
+    if (!aligned(dst, 16) || (src && !aligned(src, 16))) return UBEP_ERR_INVALID_ARG;
+    if (n_vec >= ((int64_t)1 << 36)) return UBEP_ERR_UNSUPPORTED;
+    if (n_vec == 0) return UBEP_OK;
+    return hip_status(launch_stream_probe(src, dst, n_vec, fan_in, fan_out, stream));
 }
 
 ubep_status ubep_time_next_launch(hipEvent_t start, hipEvent_t stop) {

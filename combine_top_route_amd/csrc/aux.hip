@@ -53,6 +53,55 @@ __global__ __launch_bounds__(256) void copy_kernel(const u32x4* __restrict__ src
     for (; i < n; i += stride) dst[i] = src[i];
 }
 
+// Streaming reference for the row kernels' bandwidth ceilings.  Vector i of n
+// reads FI 16-byte vectors, src[f * n + i] for f < FI, with non-temporal
+// loads (read once, as combine reads its rows), XORs them, and stores the
+// result to FO places, dst[g * n + i] for g < FO: FI + FO sequential,
+// coalesced streams.  The combine's byte mix is FI = 8, FO = 1 (eight rows
+// read per row written), the dispatch's FI = 1, FO = 8.  FI = 0 stores i
+// itself (a write stream); FO = 0 keeps the loads alive through a store to
+// dst[0] that only a fold equal to an unlikely word would make (a read
+// stream).  Two vectors per thread and iteration keep 2 * FI loads in flight.
+template <int FI, int FO>
+__global__ __launch_bounds__(256) void stream_kernel(const u32x4* __restrict__ src,
+                                                     u32x4* __restrict__ dst, int64_t n) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    u32x4 fold = {0u, 0u, 0u, 0u};
+    for (int64_t i0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i0 < n; i0 += 2 * stride) {
+        u32x4 v[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int64_t i = i0 + u * stride;
+            const int64_t ic = i < n ? i : n - 1;
+            v[u] = u32x4{(uint32_t)ic, (uint32_t)(ic >> 32), 0u, 0u};
+            if constexpr (FI > 0) {
+                u32x4 r[FI];
+#pragma unroll
+                for (int f = 0; f < FI; ++f) r[f] = __builtin_nontemporal_load(src + f * n + ic);
+                v[u] = r[0];
+#pragma unroll
+                for (int f = 1; f < FI; ++f) v[u] ^= r[f];
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int64_t i = i0 + u * stride;
+            if (i >= n) continue;
+            if constexpr (FO > 0) {
+#pragma unroll
+                for (int g = 0; g < FO; ++g) dst[g * n + i] = v[u];
+            } else {
+                fold ^= v[u];
+            }
+        }
+    }
+    if constexpr (FO == 0) {
+        if (fold[0] == 0x9E3779B9u && fold[1] == 0x7F4A7C15u && fold[2] == 0xF39CC060u &&
+            fold[3] == 0x5CEDC834u)
+            dst[0] = fold;
+    }
+}
+
 __global__ __launch_bounds__(256) void fill_zero_kernel(uint32_t* p, int64_t words) {
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < words;
          i += (int64_t)gridDim.x * blockDim.x)
@@ -85,6 +134,29 @@ hipError_t launch_copy(const void* src, void* dst, size_t bytes, hipStream_t str
     if (e != hipSuccess) return e;
     return launch_kernel(copy_kernel, dim3(grid_for(n, 256 * 4, (int64_t)di.cus * 16)), dim3(256), 0,
                          stream, static_cast<const u32x4*>(src), static_cast<u32x4*>(dst), n);
+}
+
+hipError_t launch_stream_probe(const void* src, void* dst, int64_t n, int fan_in, int fan_out,
+                               hipStream_t stream) {
+    DeviceInfo di;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    e = device_info(dev, &di);
+    if (e != hipSuccess) return e;
+    const dim3 grid(grid_for(n, 256 * 2, (int64_t)di.cus * 8)), block(256);
+    const u32x4* s = static_cast<const u32x4*>(src);
+    u32x4* d = static_cast<u32x4*>(dst);
+    switch (fan_in * 16 + fan_out) {
+        case 0 * 16 + 1: return launch_kernel(stream_kernel<0, 1>, grid, block, 0, stream, s, d, n);
+        case 1 * 16 + 0: return launch_kernel(stream_kernel<1, 0>, grid, block, 0, stream, s, d, n);
+        case 1 * 16 + 1: return launch_kernel(stream_kernel<1, 1>, grid, block, 0, stream, s, d, n);
+        case 8 * 16 + 1: return launch_kernel(stream_kernel<8, 1>, grid, block, 0, stream, s, d, n);
+        case 1 * 16 + 8: return launch_kernel(stream_kernel<1, 8>, grid, block, 0, stream, s, d, n);
+        case 8 * 16 + 0: return launch_kernel(stream_kernel<8, 0>, grid, block, 0, stream, s, d, n);
+        case 0 * 16 + 8: return launch_kernel(stream_kernel<0, 8>, grid, block, 0, stream, s, d, n);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 hipError_t launch_fill_zero(void* ws, size_t bytes, hipStream_t stream) {

@@ -49,15 +49,60 @@ struct ChunkArgs {
     uint64_t spin_ticks;
     uint32_t debug;
     int16_t order[kMaxC];
+    const int32_t* dev_order;   // not null: the order in device memory (LPT policy)
 };
+
+// LPT chunk order (imbalance-aware: the pages balance completion time rather
+// than counts).  On one GPU every chunk moves the same bytes, so a chunk's
+// load is read as its largest per-destination row count,
+//   load(c) = max over d of cd(c, d),  cd(c, d) = chunk_offset[c+1][d] - chunk_offset[c][d]
+// (rank_count[d] - chunk_offset[C-1][d] for the last chunk), and chunks go in
+// descending load, equal loads in ascending chunk id.  One workgroup: the
+// threads sweep the C x R counts (LDS max per chunk), then each chunk's place
+// is the number of chunks that precede it.
+__global__ __launch_bounds__(256) void chunk_lpt_kernel(const int32_t* __restrict__ chunk_offset,
+                                                        const int32_t* __restrict__ rank_count,
+                                                        int32_t* __restrict__ order, int32_t C,
+                                                        int32_t R) {
+    __shared__ int32_t s_load[kMaxC];
+    for (int32_t c = threadIdx.x; c < C; c += blockDim.x) s_load[c] = 0;
+    __syncthreads();
+    const int64_t n = (int64_t)C * R;
+    for (int64_t i = threadIdx.x; i < n; i += blockDim.x) {
+        const int32_t c = (int32_t)(i / R), d = (int32_t)(i - (int64_t)c * R);
+        const int32_t lo = c == 0 ? 0 : chunk_offset[i];
+        const int32_t hi = c + 1 < C ? chunk_offset[i + R] : rank_count[d];
+        atomicMax(&s_load[c], hi - lo);
+    }
+    __syncthreads();
+    for (int32_t c = threadIdx.x; c < C; c += blockDim.x) {
+        const int32_t lc = s_load[c];
+        int32_t place = 0;
+        for (int32_t o = 0; o < C; ++o) {
+            const int32_t lo_ = s_load[o];
+            place += (lo_ > lc || (lo_ == lc && o < c)) ? 1 : 0;
+        }
+        order[place] = c;
+    }
+}
+
+hipError_t launch_chunk_lpt(const Plan& p, const int32_t* chunk_offset, const int32_t* rank_count,
+                            int32_t* order, hipStream_t stream) {
+    return launch_kernel(chunk_lpt_kernel, dim3(1), dim3(256), 0, stream, chunk_offset, rank_count,
+                         order, p.C, p.R);
+}
 
 template <int G, int VPT>
 __global__ __launch_bounds__(kChunkBlock) void chunked_kernel(ChunkArgs a) {
     constexpr int TPB = kChunkBlock / G;
     __shared__ uint32_t s_ticket;
+    __shared__ int16_t s_order[kMaxC];
     const int tid = threadIdx.x;
     const int gtid = tid % G;
     uint32_t* status = &a.hdr[kHdrStatus];
+    for (int32_t i = tid; i < a.C; i += kChunkBlock)
+        s_order[i] = a.dev_order != nullptr ? (int16_t)a.dev_order[i] : a.order[i];
+    __syncthreads();
 
     // Tickets are claimed kTicketBatch at a time and processed in order; a C
     // task in a batch waits only on smaller tickets, held by running
@@ -82,7 +127,7 @@ __global__ __launch_bounds__(kChunkBlock) void chunked_kernel(ChunkArgs a) {
         uint32_t idx;
         if (ticket < L * n) {                               // the first L chunks' D tasks
             is_d = true;
-            c = a.order[ticket / n];
+            c = s_order[ticket / n];
             idx = ticket % n;
         } else {
             const uint32_t u = ticket - L * n;
@@ -90,12 +135,12 @@ __global__ __launch_bounds__(kChunkBlock) void chunked_kernel(ChunkArgs a) {
             if (pair < C - L) {                             // D(o_{pair+L}) then C(o_pair)
                 const uint32_t r = u % (2u * n);
                 is_d = r < n;
-                c = is_d ? a.order[pair + L] : a.order[pair];
+                c = is_d ? s_order[pair + L] : s_order[pair];
                 idx = is_d ? r : r - n;
             } else {                                        // the last L chunks' C tasks
                 const uint32_t v = u - (C - L) * 2u * n;
                 is_d = false;
-                c = a.order[C - L + v / n];
+                c = s_order[C - L + v / n];
                 idx = v % n;
             }
         }
@@ -144,8 +189,9 @@ __global__ __launch_bounds__(kChunkBlock) void chunked_kernel(ChunkArgs a) {
 }
 
 hipError_t launch_chunked(const Plan& p, const void* x, const int32_t* pos, const float* topk_w,
-                          void* recv, void* out, const int32_t* chunk_order, uint64_t spin_ticks,
-                          uint32_t debug_flags, void* ws, int device, hipStream_t stream) {
+                          void* recv, void* out, const int32_t* chunk_order,
+                          const int32_t* dev_order, uint64_t spin_ticks, uint32_t debug_flags,
+                          void* ws, int device, hipStream_t stream) {
     const int64_t nvec = p.H / 8;
     int G, VPT;
     pick_group(nvec, &G, &VPT);
@@ -175,6 +221,7 @@ hipError_t launch_chunked(const Plan& p, const void* x, const int32_t* pos, cons
     a.spin_ticks = spin_ticks;
     a.debug = debug_flags;
     for (int i = 0; i < kMaxC; ++i) a.order[i] = (int16_t)(i < p.C ? (chunk_order ? chunk_order[i] : i) : 0);
+    a.dev_order = dev_order;
     DeviceInfo di;
     hipError_t e = device_info(device, &di);
     if (e != hipSuccess) return e;

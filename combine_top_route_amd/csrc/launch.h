@@ -70,9 +70,15 @@ hipError_t launch_dispatch_fp8(const Plan& p, const void* x, const int32_t* pos,
 hipError_t launch_combine(const Plan& p, const void* y, const int32_t* pos, const float* topk_w,
                           void* out, uint32_t* status, hipStream_t stream);
 
+// chunk_order: host order (or null); dev_order: a device order (LPT policy) that
+// takes its place when not null.
 hipError_t launch_chunked(const Plan& p, const void* x, const int32_t* pos, const float* topk_w,
-                          void* recv, void* out, const int32_t* chunk_order, uint64_t spin_ticks,
-                          uint32_t debug_flags, void* ws, int device, hipStream_t stream);
+                          void* recv, void* out, const int32_t* chunk_order,
+                          const int32_t* dev_order, uint64_t spin_ticks, uint32_t debug_flags,
+                          void* ws, int device, hipStream_t stream);
+
+hipError_t launch_chunk_lpt(const Plan& p, const int32_t* chunk_offset, const int32_t* rank_count,
+                            int32_t* order, hipStream_t stream);
 
 hipError_t launch_gate(const ubep_gate_shape& g, const float* logits, int32_t* idx, float* w,
                        hipStream_t stream);
@@ -93,6 +99,9 @@ hipError_t launch_identity_fp8(int64_t rows, int64_t H, const uint8_t* q, const 
                                void* y, hipStream_t stream);
 
 hipError_t launch_copy(const void* src, void* dst, size_t bytes, hipStream_t stream);
+
+hipError_t launch_stream_probe(const void* src, void* dst, int64_t n, int fan_in, int fan_out,
+                               hipStream_t stream);
 
 hipError_t launch_fill_zero(void* ws, size_t bytes, hipStream_t stream);
 

@@ -14,6 +14,7 @@
 // kernel's latency.
 #include <atomic>
 #include <mutex>
+#include <type_traits>
 
 #include "launch.h"
 #include "layout_worker.h"
@@ -34,6 +35,13 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_kernel(LayoutArgs a) {
                                                                  &done);
     if (threadIdx.x == 0 && done == gridDim.x - 1u) layout_reset(a, epoch);
 }
+
+static std::atomic<int32_t> g_worker_cap{0};
+
+void set_layout_worker_cap(int32_t n) { g_worker_cap.store(n, std::memory_order_relaxed); }
+
+// No worker cap set (a cap asks for the persistent kernel, whose tiles it spreads).
+static bool g_worker_cap_default() { return g_worker_cap.load(std::memory_order_relaxed) == 0; }
 
 // ---------------------------------------------------------------- one-workgroup layout
 constexpr int kSingleThreads = 1024;
@@ -206,9 +214,6 @@ bool layout_lds_fits(const Plan& p) {
     return layout_fits_one_group(p) || layout_lds_bytes(p, kLayoutWaves) <= kLdsBytesPerCu;
 }
 
-static std::atomic<int32_t> g_worker_cap{0};
-
-void set_layout_worker_cap(int32_t n) { g_worker_cap.store(n, std::memory_order_relaxed); }
 
 // Workers of the persistent layout: enough to fill the chip (or the cap set
 // by ubep_set_layout_workers), never more than tiles, and few enough tiles
@@ -222,6 +227,185 @@ int64_t layout_workers(const Plan& p, int cus) {
     if (n < need) n = need;
     if (n > p.n_tiles) n = p.n_tiles;
     return n;
+}
+
+// ---------------------------------------------------------------- replicated layout
+// Small problems with several tiles (up to kRepMaxRows rows, e.g. a
+// 4096-token decode step of 32768 rows): every workgroup owns one tile and
+// sweeps ALL the ids itself (a few hundred KB, read from L2), counting per key
+// the rows before its tile and the rest.  That gives its tile's exclusive
+// prefixes and the key totals with no value crossing workgroups: no tickets,
+// no published words, no polling -- the round trips through device memory
+// that bound the persistent kernel at this size -- at the price of the ids
+// being read once per workgroup.  Then it ranks its own tile as the
+// persistent kernel does (per-wave counts, ballot peer masks).  Under skewed
+// routing many lanes of one atomic hit the same hot key and serialise, so
+// for up to 256 keys the counts go to four copies (by lane), summed after.
+constexpr int64_t kRepMaxRows = 32768;
+constexpr int kRepMaxK = 1024;
+constexpr int kRepMaxSlice = 1024;
+constexpr int kRepMaxTiles = 256;
+
+bool layout_replicates(const Plan& p, const int32_t* idx) {
+    const int32_t K = p.order ? p.E : p.R;
+    const int64_t e_per = (p.E + p.n_tiles - 1) / p.n_tiles;
+    return g_worker_cap_default() && p.rows <= kRepMaxRows && p.rows % 4 == 0 &&
+           ((uintptr_t)idx % 16) == 0 && p.n_tiles >= 2 && p.n_tiles <= kRepMaxTiles &&
+           K <= kRepMaxK && e_per <= kRepMaxSlice;
+}
+
+template <int LR, int NV, bool EORD>
+__global__ __launch_bounds__(kLayoutThreads) void layout_replicated_kernel(LayoutArgs a) {
+    // [copy][0][q]: rows with key q before this tile; [copy][1][q]: the others
+    __shared__ int32_t s_hist[2 * kRepMaxK];
+    __shared__ int32_t s_off[kRepMaxK];            // exclusive scan of the key totals
+    __shared__ int32_t s_wh[kLayoutWaves * kRepMaxK];   // this tile's per-wave key counts, then row bases
+    __shared__ int32_t s_eh[kRepMaxSlice];         // expert counts of this workgroup's slice (rank order)
+    __shared__ int32_t s_tmp[kLayoutWaves];
+    constexpr int T_ = kLayoutThreads;
+    const Plan& p = a.p;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int64_t tile = blockIdx.x;
+    const int64_t t_start = tile * p.tile_rows;
+    const int32_t R = p.R, E = p.E, epr = p.epr;
+    const int32_t K = EORD ? E : R;
+    const int32_t e_per = (E + (int32_t)gridDim.x - 1) / (int32_t)gridDim.x;
+    const int32_t e_lo = (int64_t)tile * e_per < E ? (int32_t)tile * e_per : E;
+    const int32_t n_e = EORD ? 0 : (E - e_lo < e_per ? E - e_lo : e_per);
+    const int32_t copies = K <= kRepMaxK / 4 ? 4 : 1;    // both fit s_hist
+    const int32_t my_copy = (tid & (copies - 1)) * 2 * K;
+
+    // this tile's ids first, then the sweep over every row (int4 loads, all in
+    // flight together; clamped, so every address is valid)
+    int32_t ev[LR];
+    load_ids<kLayoutWaves, LR>(a, tile, ev);
+    const int4* src = reinterpret_cast<const int4*>(a.idx);
+    const int64_t n4 = p.rows / 4;
+    int4 v[NV];
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+        const int64_t i = tid + (int64_t)j * T_;
+        v[j] = src[i < n4 ? i : n4 - 1];
+    }
+    for (int i = tid; i < 2 * K * copies; i += T_) s_hist[i] = 0;
+    for (int i = tid; i < kLayoutWaves * K; i += T_) s_wh[i] = 0;
+    for (int i = tid; i < n_e; i += T_) s_eh[i] = 0;
+    __syncthreads();
+
+    const auto count_row = [&](int64_t row, int32_t e) {
+        if ((uint32_t)e >= (uint32_t)E) e = 0;            // as the other modes: expert 0 (reported below)
+        const uint32_t q = EORD ? (uint32_t)e : rank_of((uint32_t)e, p.epr_magic);
+        atomicAdd(&s_hist[my_copy + (row < t_start ? 0 : K) + (int32_t)q], 1);
+        if (!EORD && (uint32_t)(e - e_lo) < (uint32_t)n_e) atomicAdd(&s_eh[e - e_lo], 1);
+    };
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+        const int64_t i = tid + (int64_t)j * T_;
+        if (i < n4) {
+            count_row(4 * i, v[j].x);
+            count_row(4 * i + 1, v[j].y);
+            count_row(4 * i + 2, v[j].z);
+            count_row(4 * i + 3, v[j].w);
+        }
+    }
+    // this tile's per-wave key counts
+    bool bad = false, bad_pos = false;
+    check_ids<kLayoutWaves, LR>(p, ev, &bad);
+    {
+        int64_t lo, hi;
+        wave_rows<kLayoutWaves>(p, w, &lo, &hi);
+#pragma unroll
+        for (int i = 0; i < LR; ++i) {
+            if (lo + 64 * i + lane < hi) {
+                const uint32_t e = (uint32_t)ev[i];
+                atomicAdd(&s_wh[w * K + (EORD ? (int32_t)e : (int32_t)rank_of(e, p.epr_magic))], 1);
+            }
+        }
+    }
+    __syncthreads();
+    if (copies > 1) {
+        for (int i = tid; i < 2 * K; i += T_)
+            s_hist[i] += s_hist[2 * K + i] + s_hist[4 * K + i] + s_hist[6 * K + i];
+        __syncthreads();
+    }
+
+    {   // exclusive scan of the key totals; thread i owns a run of keys
+        const int per = (K + T_ - 1) / T_;
+        int32_t mine = 0;
+        for (int i = 0; i < per; ++i) {
+            const int32_t d = tid * per + i;
+            if (d < K) mine += s_hist[d] + s_hist[K + d];
+        }
+        int32_t inc = mine;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int32_t u = __shfl_up(inc, o, 64);
+            if (lane >= o) inc += u;
+        }
+        if (lane == 63) s_tmp[w] = inc;
+        __syncthreads();
+        int32_t run = inc - mine;
+        for (int i = 0; i < w; ++i) run += s_tmp[i];
+        for (int i = 0; i < per; ++i) {
+            const int32_t d = tid * per + i;
+            if (d < K) {
+                s_off[d] = run;
+                run += s_hist[d] + s_hist[K + d];
+            }
+        }
+    }
+    __syncthreads();
+    // row bases of each wave of this tile: region start + rows in earlier
+    // tiles + rows of earlier waves of this tile
+    for (int32_t d = tid; d < K; d += T_) {
+        int32_t run = s_off[d] + s_hist[d];
+#pragma unroll
+        for (int v_ = 0; v_ < kLayoutWaves; ++v_) {
+            const int32_t c = s_wh[v_ * K + d];
+            s_wh[v_ * K + d] = run;
+            run += c;
+        }
+    }
+    __syncthreads();
+    int32_t q[LR];
+    tile_ranks<kLayoutWaves, LR, EORD>(p, ev, s_wh, q);
+    store_positions<kLayoutWaves, LR, false>(a, tile, q, &bad_pos);
+
+    // rows with a key of rank d in a per-key array v (rank order: v[d])
+    const auto rank_sum = [&](const int32_t* v_, int32_t d) -> int32_t {
+        if (!EORD) return v_[d];
+        int32_t c = 0;
+        for (int32_t e = d * epr; e < (d + 1) * epr; ++e) c += v_[e];
+        return c;
+    };
+    const int64_t tok0 = tile * p.tile_tokens;
+    if (tok0 % p.tps == 0)
+        for (int32_t d = tid; d < R; d += T_) a.send_offset[(tok0 / p.tps) * R + d] = rank_sum(s_hist, d);
+    if (a.chunk_offset != nullptr && tok0 % p.tpc == 0)
+        for (int32_t d = tid; d < R; d += T_) a.chunk_offset[(tok0 / p.tpc) * R + d] = rank_sum(s_hist, d);
+    for (int i = tid; i < n_e; i += T_) a.expert_count[e_lo + i] = s_eh[i];
+    if (tile == 0) {
+        for (int32_t d = tid; d < R; d += T_) {
+            int32_t c = 0;
+            if (!EORD) {
+                c = s_hist[K + d];                         // tile 0: every row is "not before"
+            } else {
+                for (int32_t e = d * epr; e < (d + 1) * epr; ++e) c += s_hist[K + e];
+            }
+            a.rank_count[d] = c;
+            a.recv_offset[d] = s_off[EORD ? d * epr : d];
+        }
+        if (tid == 0) a.recv_offset[R] = (int32_t)p.rows;
+        if (EORD) {
+            for (int32_t e = tid; e < E; e += T_) {
+                a.expert_count[e] = s_hist[K + e];
+                if (a.expert_offset != nullptr) a.expert_offset[e] = s_off[e];
+            }
+            if (tid == 0 && a.expert_offset != nullptr) a.expert_offset[E] = (int32_t)p.rows;
+        }
+    }
+    if (bad) raise_status(a.status, UBEP_ERR_BAD_EXPERT_ID);
+    if (bad_pos) raise_status(a.status, UBEP_ERR_BAD_POSITION);
 }
 
 // ---------------------------------------------------------------- allocation-free layout
@@ -286,8 +470,28 @@ hipError_t launch_layout(const Plan& p, const int32_t* idx, int32_t* pos, int32_
             return launch_kernel(layout_single_kernel<32>, dim3(1), dim3(kSingleThreads), 0, stream, a);
         return launch_kernel(layout_single_kernel<64>, dim3(1), dim3(kSingleThreads), 0, stream, a);
     }
-    const int64_t lds = layout_lds_bytes(p, kLayoutWaves);
     const int64_t lane_rows = (p.tile_rows + kLayoutThreads - 1) / kLayoutThreads;
+    if (layout_replicates(p, idx)) {
+        const int64_t nv = (p.rows / 4 + kLayoutThreads - 1) / kLayoutThreads;
+        const auto rep = [&](auto lr_tag) -> hipError_t {
+            constexpr int LR_ = decltype(lr_tag)::value;
+            const dim3 g((unsigned)p.n_tiles), b(kLayoutThreads);
+            if (p.order != 0) {
+                if (nv <= 4) return launch_kernel(layout_replicated_kernel<LR_, 4, true>, g, b, 0, stream, a);
+                if (nv <= 8) return launch_kernel(layout_replicated_kernel<LR_, 8, true>, g, b, 0, stream, a);
+                return launch_kernel(layout_replicated_kernel<LR_, 16, true>, g, b, 0, stream, a);
+            }
+            if (nv <= 4) return launch_kernel(layout_replicated_kernel<LR_, 4, false>, g, b, 0, stream, a);
+            if (nv <= 8) return launch_kernel(layout_replicated_kernel<LR_, 8, false>, g, b, 0, stream, a);
+            return launch_kernel(layout_replicated_kernel<LR_, 16, false>, g, b, 0, stream, a);
+        };
+        static_assert(kRepMaxRows / 4 <= 16 * kLayoutThreads, "vectors per thread");
+        if (lane_rows <= 1) return rep(std::integral_constant<int, 1>{});
+        if (lane_rows <= 2) return rep(std::integral_constant<int, 2>{});
+        if (lane_rows <= 4) return rep(std::integral_constant<int, 4>{});
+        return rep(std::integral_constant<int, 8>{});
+    }
+    const int64_t lds = layout_lds_bytes(p, kLayoutWaves);
     const auto go = [&](void (*kernel)(LayoutArgs)) -> hipError_t {
         if (lds > 64 * 1024) {
             const hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),

@@ -89,6 +89,7 @@ struct Plan {
     size_t off_wbase;      // int32  [n_tiles][8][K] rows with key q in earlier waves of the tile
     size_t off_flags;      // uint32 [C][kFlagStride] chunk ready flags
     size_t ws_bytes;
+    size_t off_order;      // int32  [C] chunk order computed on the device (LPT policy)
     // Position keys (last, so that the fields the rank-order kernels read keep
     // their places).  Rank order: rows sort by (rank, token, slot), one key
     // per rank.  Expert order: rows sort by (expert, token, slot), one key per

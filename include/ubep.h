@@ -34,9 +34,13 @@
  *     and returns UBEP_OK without synchronising.  Errors found by a kernel
  *     (bad expert id, bad position, wait time-out) are recorded in the
  *     workspace's device status word; read them with ubep_get_device_status.
- *   - The library keeps no mutable global state; calls are thread-safe as long
- *     as concurrent calls use different workspaces.  Calls that share one
- *     workspace must be ordered on one stream.
+ *   - Calls keep no state between them, except: the per-GPU static array of
+ *     ubep_layout_noalloc (see there); read-only caches of device properties
+ *     and occupancy; and the two controls of ubep_testing.h (a process-wide
+ *     cap on layout workgroups and a per-thread pending pair of timing
+ *     events), which only tests, tuning and timing use.  Calls are
+ *     thread-safe as long as concurrent calls use different workspaces.
+ *     Calls that share one workspace must be ordered on one stream.
  */
 #ifndef UBEP_H
 #define UBEP_H
@@ -50,7 +54,7 @@
 extern "C" {
 #endif
 
-#define UBEP_ABI_VERSION 1
+#define UBEP_ABI_VERSION 2
 
 /* Problem shape (host struct).  Constraints checked by ubep_check_shape:
  * every field > 0; k <= E; k <= 32; E % R == 0; T % R == 0; T % C == 0;
@@ -255,13 +259,22 @@ ubep_status ubep_combine(const ubep_shape *shape /*host*/, const void *y, const 
 /* Chunked dispatch + combine in one persistent kernel, for identity experts and
  * a bf16 payload (y = recv).  Tokens form C contiguous chunks.  Work is handed
  * out from one task counter in the order D(o0), D(o1), C(o0), D(o2), C(o1), ...,
- * C(o_{C-1}) for the chunk order o = chunk_order (host array of C distinct
- * chunk ids; NULL means 0..C-1).  D(c) dispatches chunk c and then raises the
+ * C(o_{C-1}) for a chunk order o.  D(c) dispatches chunk c and then raises the
  * chunk's ready flag in HBM; C(c) polls that flag instead of waiting at a
  * global barrier ("Kernel Decomposition": asynchronous peer-to-peer signalling
  * through global memory) and then combines chunk c.  recv and out receive the
  * same bytes as ubep_dispatch(UBEP_BF16) followed by ubep_combine(y = recv),
  * for every chunk order.
+ * The order (pass at most one of the two forms):
+ *   chunk_order  host array of C distinct chunk ids, or NULL;
+ *   chunk_offset, rank_count  ubep_layout's outputs on the device ([C][R],
+ *                may be NULL when C == 1, and [R]): the chunks then run in
+ *                the imbalance-aware order of ubep_chunk_order_lpt, computed
+ *                on the device by one small kernel before the pipeline (no
+ *                host synchronisation; "Hierarchical Token-Level Scheduling"
+ *                and "Latency Homogenization" balance completion time rather
+ *                than counts);
+ *   all NULL     chunks 0..C-1.
  * spin_limit_ns bounds each flag wait (0 selects one second); an expired wait
  * sets UBEP_ERR_TIMEOUT (unless the status word already holds an error),
  * abandons that wait, makes every later wait of the call give up at once,
@@ -273,8 +286,18 @@ ubep_status ubep_combine(const ubep_shape *shape /*host*/, const void *y, const 
 ubep_status ubep_dispatch_combine_chunked(const ubep_shape *shape /*host*/, const void *x,
                                           const int32_t *pos, const float *topk_w, void *recv,
                                           void *out, const int32_t *chunk_order /*host*/,
+                                          const int32_t *chunk_offset, const int32_t *rank_count,
                                           uint64_t spin_limit_ns, uint32_t debug_flags,
                                           void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Imbalance-aware (LPT) chunk order, on the device.  On one GPU every chunk
+ * moves the same number of rows, so a chunk's load is taken as its largest
+ * per-rank row count, load(c) = max over d of (rows of chunk c to rank d),
+ * from ubep_layout's chunk_offset [C][R] and rank_count [R] (chunk_offset may
+ * be NULL when C == 1).  order [C] (int32, device) receives the chunk ids in
+ * descending load, equal loads in ascending id.  One workgroup on `stream`. */
+ubep_status ubep_chunk_order_lpt(const ubep_shape *shape /*host*/, const int32_t *chunk_offset,
+                                 const int32_t *rank_count, int32_t *order, hipStream_t stream);
 
 /* Dispatch + combine in one persistent kernel with token-granular readiness
  * carried by the data ("Data-as-Flag", its sentinel-polling variant: the
@@ -364,24 +387,17 @@ ubep_status ubep_identity_expert_fp8(int64_t rows, int64_t H, const uint8_t *q,
  * pointers); the bandwidth and counter-calibration reference. */
 ubep_status ubep_copy(const void *src, void *dst, size_t bytes, hipStream_t stream);
 
-/* Profiling aid: the next kernel that a ubep_* call launches from this host
- * thread records `start` when it begins and `stop` when it ends.  The events
- * are written by that kernel's own dispatch (hipExtLaunchKernel), so no marker
- * packet sits between kernels; hipEventElapsedTime(start, stop) is then the
- * kernel's duration.  Every entry point above launches one kernel, except
- * ubep_layout_dispatch when it falls back to two launches (the first is
- * timed).  The pair stays pending until a launch takes it, also across calls
- * that fail validation.  Both null: clear a pending pair; exactly one null:
- * UBEP_ERR_INVALID_ARG.  The events must have been created by the caller. */
-ubep_status ubep_time_next_launch(hipEvent_t start, hipEvent_t stop);
-
-/* Process-wide cap on the number of layout workgroups of later ubep_layout /
- * ubep_layout_dispatch calls (n >= 1), or 0 for the default (two per compute
- * unit, at most one per tile).  The layout still launches at least as many
- * workgroups as its per-workgroup tile limit needs, so every result is the
- * same; a small cap makes workgroups take several tiles (a tuning and
- * testing control).  n < 0: UBEP_ERR_INVALID_ARG. */
-ubep_status ubep_set_layout_workers(int32_t n);
+/* Bandwidth reference of the row kernels (not part of the path): n_vec
+ * 16-byte vectors, each the XOR of fan_in vectors read with non-temporal
+ * loads, src[f * n_vec + i] for f < fan_in, stored to fan_out places,
+ * dst[g * n_vec + i] for g < fan_out -- fan_in + fan_out sequential streams.
+ * fan_in, fan_out in {0, 1, 8}, not both 0: (8, 1) is combine's byte mix
+ * (eight rows read per row written), (1, 8) dispatch's; fan_in = 0 stores
+ * the index itself (a write stream); fan_out = 0 reads only (dst needs 16
+ * bytes and is almost never written).  Reads 16 * fan_in * n_vec bytes and
+ * writes 16 * fan_out * n_vec bytes; 16-byte aligned pointers. */
+ubep_status ubep_stream_probe(const void *src, void *dst, int64_t n_vec, int fan_in, int fan_out,
+                              hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -1,5 +1,5 @@
 """The C-ABI library without a GPU: it loads, exports every function that
-include/ubep.h declares, and its host-side validation rejects bad arguments
+include/*.h declares, and its host-side validation rejects bad arguments
 before anything is enqueued (no HIP call is reached on these paths)."""
 import ctypes as C
 import os
@@ -13,7 +13,8 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
 def _declared():
-    src = open(os.path.join(ROOT, "include", "ubep.h")).read()
+    src = "".join(open(os.path.join(ROOT, "include", h)).read()
+                  for h in sorted(os.listdir(os.path.join(ROOT, "include"))) if h.endswith(".h"))
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
     return sorted(set(re.findall(r"\b(ubep_[a-z0-9_]+)\s*\(", src)))
 
@@ -29,7 +30,7 @@ def test_library_exports_every_declared_symbol():
     L = C.CDLL(ubep.LIB_PATH)
     missing = [n for n in _declared() if not hasattr(L, n)]
     assert not missing, missing
-    assert ubep.ubep_abi_version() == 1
+    assert ubep.ubep_abi_version() == 2
 
 
 def test_shape_validation():
@@ -88,10 +89,19 @@ def test_validation_happens_before_any_launch():
     order = (C.c_int32 * 2)(0, 0)
     s2 = ubep.ubep_shape(8, 64, 4, 2, 2, 2)
     nws = L.ubep_workspace_bytes(C.byref(s2))
-    assert L.ubep_dispatch_combine_chunked(C.byref(s2), 16, 16, 16, 16, 16, order, 0, 0, 256, nws,
-                                           None) == ubep.ERR_INVALID_ARG
-    assert L.ubep_dispatch_combine_chunked(C.byref(s2), 16, 16, 16, 16, 16, None, 0, 4, 256, nws,
-                                           None) == ubep.ERR_INVALID_ARG   # unknown debug flag
+    assert L.ubep_dispatch_combine_chunked(C.byref(s2), 16, 16, 16, 16, 16, order, None, None, 0,
+                                           0, 256, nws, None) == ubep.ERR_INVALID_ARG
+    assert L.ubep_dispatch_combine_chunked(C.byref(s2), 16, 16, 16, 16, 16, None, None, None, 0, 4,
+                                           256, nws, None) == ubep.ERR_INVALID_ARG  # unknown flag
+    good = (C.c_int32 * 2)(1, 0)
+    assert L.ubep_dispatch_combine_chunked(C.byref(s2), 16, 16, 16, 16, 16, good, 256, 256, 0, 0,
+                                           256, nws, None) == ubep.ERR_INVALID_ARG  # two orders
+    assert L.ubep_dispatch_combine_chunked(C.byref(s2), 16, 16, 16, 16, 16, None, None, 256, 0, 0,
+                                           256, nws, None) == ubep.ERR_INVALID_ARG  # no chunk_offset
+    assert L.ubep_dispatch_combine_chunked(C.byref(s2), 16, 16, 16, 16, 16, None, 256, None, 0, 0,
+                                           256, nws, None) == ubep.ERR_INVALID_ARG  # no rank_count
+    assert L.ubep_chunk_order_lpt(C.byref(s2), None, 256, 256, None) == ubep.ERR_INVALID_ARG
+    assert L.ubep_chunk_order_lpt(C.byref(s2), 256, 256, None, None) == ubep.ERR_INVALID_ARG
     assert L.ubep_dispatch_combine_sentinel(C.byref(s2), 16, 16, 16, 16, 16, 0, 4, 256, nws,
                                             None) == ubep.ERR_INVALID_ARG  # unknown debug flag
     assert ubep.status_str(ubep.ERR_TIMEOUT) == "ready-flag wait timed out"

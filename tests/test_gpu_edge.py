@@ -13,6 +13,7 @@ import oracle
 from combine_top_route_amd.buffers import alloc_buffers, run_path
 from workloads import custom
 from gpu_helpers import assert_layout_equal, device_status, gpu_layout, say, to_np, upload
+from gpu_helpers import workload as workload_full
 
 pytestmark = pytest.mark.gpu
 
@@ -181,7 +182,49 @@ def test_chunked_gives_up_after_one_limit_whatever_the_status():
     np.testing.assert_array_equal(to_np(b.out), out)
 
 
-@pytest.mark.parametrize("order", ["identity", "reversed", "lpt", "random"])
+def _lpt_by_definition(L):
+    """Chunks by descending largest per-rank row count, ties to the lower id."""
+    cd = np.diff(np.vstack([L["chunk_offset"], L["rank_count"][None]]), axis=0)   # [C, R]
+    return sorted(range(cd.shape[0]), key=lambda c: (-int(cd[c].max()), c))
+
+
+LPT_SPECS = [dict(T=2048, H=8, E=64, k=8, R=16, C=16, routing="zipf", seed=4),
+             dict(T=4096, H=8, E=256, k=8, R=32, C=256, routing="zipf", seed=7),   # many ties
+             dict(T=960, H=8, E=24, k=5, R=6, C=5, routing="topk", seed=8),
+             dict(T=512, H=8, E=16, k=3, R=4, C=1, routing="topk", seed=9)]
+
+
+@pytest.mark.parametrize("spec", LPT_SPECS, ids=lambda s: f"T{s['T']}R{s['R']}C{s['C']}")
+def test_chunk_order_lpt_matches_definition(spec):
+    w = custom(**spec)
+    s = w.shape
+    b = upload(w)
+    say(f"LPT order {spec}")
+    got = gpu_layout(b)
+    order = torch.full((s.C,), -1, dtype=torch.int32, device="cuda")
+    ubep.ubep_chunk_order_lpt(s.as_dict(), b.chunk_offset if s.C > 1 else None, b.rank_count, order)
+    torch.cuda.synchronize()
+    L = oracle.layout(w.topk_idx, s.E, s.R, s.C)
+    assert_layout_equal(got, L, s.C)
+    assert to_np(order).tolist() == _lpt_by_definition(L)
+
+
+def test_chunk_order_lpt_large_prefill():
+    w = workload_full("prefill_grouped_zipf_T65536_H7168_E256_k8_R64_C16")
+    s = w.shape
+    b = alloc_buffers(dict(s.as_dict(), H=8), ubep.BF16, topk_idx=w.topk_idx)
+    say("LPT order, 65536-token prefill")
+    gpu_layout(b)
+    order = torch.full((s.C,), -1, dtype=torch.int32, device="cuda")
+    ubep.ubep_chunk_order_lpt(s.as_dict(), b.chunk_offset, b.rank_count, order)
+    torch.cuda.synchronize()
+    L = oracle.layout(w.topk_idx, s.E, s.R, s.C)
+    want = _lpt_by_definition(L)
+    assert to_np(order).tolist() == want
+    assert want != list(range(s.C))                  # skew makes the order differ from identity
+
+
+@pytest.mark.parametrize("order", ["identity", "reversed", "lpt", "random", "lpt-device"])
 def test_chunked_order_invariance(order):
     w = custom(T=2048, H=1024, E=64, k=8, R=16, C=16, routing="zipf", seed=4)
     s = w.shape
@@ -191,8 +234,9 @@ def test_chunked_order_invariance(order):
     elif order == "reversed":
         o = list(range(15, -1, -1))
     elif order == "lpt":
-        cd = np.diff(np.vstack([L["chunk_offset"], L["rank_count"][None]]), axis=0)   # [C, R]
-        o = sorted(range(16), key=lambda c: (-int(cd[c].max()), c))
+        o = _lpt_by_definition(L)
+    elif order == "lpt-device":
+        o = "lpt"
     else:
         o = list(np.random.default_rng(2).permutation(16))
     b = upload(w)

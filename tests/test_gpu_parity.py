@@ -155,8 +155,9 @@ def test_full_size_fused_layout_dispatch_whole_output(name):
     _check_full_path(name, fused=True)
 
 
-def test_large_prefill_chunked_whole_output():
-    _check_full_path("prefill_grouped_zipf_T65536_H7168_E256_k8_R64_C16", chunked=True)
+@pytest.mark.parametrize("order", [None, "lpt"], ids=["index-order", "lpt-order"])
+def test_large_prefill_chunked_whole_output(order):
+    _check_full_path("prefill_grouped_zipf_T65536_H7168_E256_k8_R64_C16", chunked=True, order=order)
 
 
 def test_fp8_codec_on_every_bf16_value():
