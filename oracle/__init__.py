@@ -15,7 +15,8 @@ import os
 import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(HERE, "liboracle.so")
+# ORACLE_LIB: another build of oracle.c (the sanitizer run of the tests)
+_LIB_PATH = os.environ.get("ORACLE_LIB") or os.path.join(HERE, "liboracle.so")
 
 OK, INVALID_ARG, UNSUPPORTED, BAD_EXPERT_ID = 0, 1, 2, 3
 
