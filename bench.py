@@ -272,10 +272,11 @@ def measure(name: str, args, hev) -> dict:
         yexp = torch.empty((s.T * s.k, s.H), dtype=torch.bfloat16, device="cuda")
     if args.mode == "fused":
         calls = ["layout_dispatch", "combine"]
-    gated = args.mode == "gated"
+    gated = args.mode in ("gated", "gate_layout")
     if gated:
         from workloads import router_logits
-        calls = ["gate"] + calls
+        calls = (["gate"] + calls if args.mode == "gated"
+                 else ["gate_layout"] + [c for c in calls if c != "layout"])
         logits = torch.from_numpy(router_logits(w.recipe)).cuda()
         grouped = w.recipe.routing == "group_zipf"
         gate_args = dict(groups=w.recipe.n_groups if grouped else 1,
@@ -287,6 +288,10 @@ def measure(name: str, args, hev) -> dict:
         st = torch.cuda.current_stream()    # the capture stream while a graph records
         if cname == "gate":
             ubep.ubep_gate(s.T, s.E, s.k, logits, b.topk_idx, b.topk_w, stream=st, **gate_args)
+        elif cname == "gate_layout":
+            ubep.ubep_gate_layout(sd, logits, b.topk_idx, b.topk_w, b.pos, b.expert_count,
+                                  b.rank_count, b.recv_offset, b.send_offset, chunk_off, None, b.ws,
+                                  stream=st, **gate_args)
         elif cname == "layout" and order == "expert":
             ubep.ubep_layout_grouped(sd, b.topk_idx, b.pos, b.expert_count, expert_off, b.rank_count,
                                      b.recv_offset, b.send_offset, chunk_off, None, b.ws, st)
@@ -350,7 +355,7 @@ def measure(name: str, args, hev) -> dict:
         step(c)
     torch.cuda.synchronize()
     per_call = {n: statistics.median(elapsed_us(c[n]) for c in cal) for n in calls}
-    dom = max((n for n in calls if n not in ("layout", "gate")), key=lambda n: per_call[n])
+    dom = max((n for n in calls if n not in ("layout", "gate", "gate_layout")), key=lambda n: per_call[n])
     if dom == "layout_dispatch":
         dom = "combine"      # the fused launch also holds the layout's latency chain
 
@@ -503,7 +508,8 @@ def summarize(m: dict, headline: str) -> dict:
     for n_, us in m["per_call"].items():
         key = {"layout_dispatch": "dispatch"}.get(n_, n_)
         by = (nb["dispatch"] + nb["combine"] if n_ in ("chunked", "sentinel")
-              else nb["layout"] + nb["dispatch"] if n_ == "layout_dispatch" else nb.get(key, 0))
+              else nb["layout"] + nb["dispatch"] if n_ == "layout_dispatch"
+              else nb["gate"] + nb["layout"] if n_ == "gate_layout" else nb.get(key, 0))
         kernels[n_] = {"us": round(us, 2), "bytes": by,
                        "GBs": round(by / (us * 1e-6) / 1e9, 1) if by else None}
     o_ms = m["passes"][other][0]
@@ -540,9 +546,12 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=None, help="workload name (default: DeepSeek-V3 decode)")
-    ap.add_argument("--mode", choices=["unfused", "chunked", "sentinel", "gated", "fused", "moe"],
+    ap.add_argument("--mode", choices=["unfused", "chunked", "sentinel", "gated", "gate_layout",
+                                       "fused", "moe"],
                     default="unfused",
                     help="gated: the step starts from router logits (ubep_gate, then unfused); "
+                         "gate_layout: the same step with ubep_gate_layout (the gate's "
+                         "selections feed the layout's counts), then dispatch and combine; "
                          "fused: ubep_layout_dispatch (one launch), then combine; "
                          "sentinel: layout, then ubep_dispatch_combine_sentinel (token-granular "
                          "readiness polled in the rows); moe: expert-grouped layout, dispatch, "

@@ -74,6 +74,8 @@ def lib() -> C.CDLL:
             "ubep_layout_noalloc": ([S, P, P, P, P, P, P, P, P, P, C.c_int, P], C.c_int),
             "ubep_layout_grouped": ([S, P, P, P, P, P, P, P, P, P, P, SZ, P], C.c_int),
             "ubep_gate": ([C.POINTER(ubep_gate_shape), P, P, P, P], C.c_int),
+            "ubep_gate_layout": ([C.POINTER(ubep_gate_shape), S, P, P, P, P, P, P, P, P, P, P, P, SZ,
+                                  P], C.c_int),
             "ubep_layout_dispatch": ([S, P, P, P, P, P, P, P, P, P, P, P, SZ, P], C.c_int),
             "ubep_dispatch": ([S, C.c_int, P, P, P, P, P, SZ, P], C.c_int),
             "ubep_combine": ([S, P, P, P, P, P, SZ, P], C.c_int),
@@ -159,6 +161,18 @@ def ubep_gate(T, E, k, logits, topk_idx, topk_w, groups=1, keep_groups=1, norm=G
     g = ubep_gate_shape(T, E, k, groups, keep_groups, norm)
     _check(lib().ubep_gate(C.byref(g), _ptr(logits), _ptr(topk_idx), _ptr(topk_w), _stream(stream)),
            "ubep_gate")
+
+
+def ubep_gate_layout(shape, logits, topk_idx, topk_w, pos, expert_count, rank_count, recv_offset,
+                     send_offset, chunk_offset, recv_src, ws, groups=1, keep_groups=1,
+                     norm=GATE_SOFTMAX, stream=None):
+    s = _shape(shape)
+    g = ubep_gate_shape(s.T, s.E, s.k, groups, keep_groups, norm)
+    _check(lib().ubep_gate_layout(C.byref(g), C.byref(s), _ptr(logits), _ptr(topk_idx),
+                                  _ptr(topk_w), _ptr(pos), _ptr(expert_count), _ptr(rank_count),
+                                  _ptr(recv_offset), _ptr(send_offset), _ptr(chunk_offset),
+                                  _ptr(recv_src), _ptr(ws), _nbytes(ws), _stream(stream)),
+           "ubep_gate_layout")
 
 
 def ubep_layout(shape, topk_idx, pos, expert_count, rank_count, recv_offset, send_offset,

@@ -77,6 +77,10 @@ void make_plan(const ubep_shape& s, Plan* p, int order) {
     off = align_up(off + (size_t)s.C * kFlagStride * 4, 256);
     p->off_order = off;
     off = align_up(off + (size_t)s.C * 4, 256);
+    p->off_gate_rank = off;
+    off = align_up(off + (size_t)p->n_tiles * s.R * 4, 256);
+    p->off_gate_expert = off;
+    off = align_up(off + (size_t)p->n_tiles * s.E * 4, 256);
     p->ws_bytes = off;
 }
 
@@ -250,8 +254,8 @@ ubep_status ubep_layout_dispatch(const ubep_shape* s, const int32_t* topk_idx, c
                                              ws, ticks, stream));
 }
 
-ubep_status ubep_gate(const ubep_gate_shape* g, const float* logits, int32_t* topk_idx,
-                      float* topk_w, hipStream_t stream) {
+static ubep_status check_gate(const ubep_gate_shape* g, const float* logits, const int32_t* topk_idx,
+                              const float* topk_w) {
     if (g == nullptr || !logits || !topk_idx || !topk_w) return UBEP_ERR_INVALID_ARG;
     if (g->T <= 0 || g->E <= 0 || g->k <= 0 || g->groups <= 0 || g->keep_groups <= 0)
         return UBEP_ERR_INVALID_ARG;
@@ -262,7 +266,53 @@ ubep_status ubep_gate(const ubep_gate_shape* g, const float* logits, int32_t* to
     if (g->T * (int64_t)g->k >= ((int64_t)1 << 31) || g->T * (int64_t)g->E >= ((int64_t)1 << 40))
         return UBEP_ERR_UNSUPPORTED;
     if (!aligned(logits, 4) || !aligned(topk_idx, 4) || !aligned(topk_w, 4)) return UBEP_ERR_INVALID_ARG;
+    return UBEP_OK;
+}
+
+ubep_status ubep_gate(const ubep_gate_shape* g, const float* logits, int32_t* topk_idx,
+                      float* topk_w, hipStream_t stream) {
+    const ubep_status st = check_gate(g, logits, topk_idx, topk_w);
+    if (st != UBEP_OK) return st;
     return hip_status(launch_gate(*g, logits, topk_idx, topk_w, stream));
+}
+
+ubep_status ubep_gate_layout(const ubep_gate_shape* g, const ubep_shape* s, const float* logits,
+                             int32_t* topk_idx, float* topk_w, int32_t* pos, int32_t* expert_count,
+                             int32_t* rank_count, int32_t* recv_offset, int32_t* send_offset,
+                             int32_t* chunk_offset, int32_t* recv_src, void* ws, size_t ws_bytes,
+                             hipStream_t stream) {
+    ubep_status st = check_gate(g, logits, topk_idx, topk_w);
+    if (st != UBEP_OK) return st;
+    Plan p;
+    st = check_and_plan(s, UBEP_BF16, &p);
+    if (st != UBEP_OK) return st;
+    if (g->T != s->T || g->E != s->E || g->k != s->k) return UBEP_ERR_INVALID_ARG;
+    if (!pos || !expert_count || !rank_count || !recv_offset || !send_offset || !ws)
+        return UBEP_ERR_INVALID_ARG;
+    if (ws_bytes < p.ws_bytes || !aligned(ws, 256)) return UBEP_ERR_INVALID_ARG;
+    if (!gate_counts_fit(*g, logits, p.tile_tokens) || !layout_from_counts_fits(p)) {
+        // shapes outside the counting kernels: the same results from two calls
+        const hipError_t e = launch_gate(*g, logits, topk_idx, topk_w, stream);
+        if (e != hipSuccess) return UBEP_ERR_HIP;
+        uint64_t ticks;
+        const ubep_status ts = spin_ticks_for(0, &ticks);
+        if (ts != UBEP_OK) return ts;
+        return hip_status(launch_layout(p, topk_idx, pos, expert_count, nullptr, rank_count,
+                                        recv_offset, send_offset, chunk_offset, recv_src, ws, ticks,
+                                        stream));
+    }
+    char* base = static_cast<char*>(ws);
+    GateCountArgs c;
+    c.rank_cnt = reinterpret_cast<int32_t*>(base + p.off_gate_rank);
+    c.expert_cnt = reinterpret_cast<int32_t*>(base + p.off_gate_expert);
+    c.tile_tokens = p.tile_tokens;
+    c.R = p.R;
+    c.epr_magic = p.epr_magic;
+    const hipError_t e = launch_gate_counting(*g, logits, topk_idx, topk_w, &c, stream);
+    if (e != hipSuccess) return UBEP_ERR_HIP;
+    return hip_status(launch_layout_from_counts(p, topk_idx, pos, expert_count, rank_count,
+                                                recv_offset, send_offset, chunk_offset, recv_src,
+                                                ws, stream));
 }
 
 ubep_status ubep_dispatch(const ubep_shape* s, int dtype, const void* x, const int32_t* pos,

@@ -4,13 +4,15 @@
 // gate selects).  The selection rule, group filter and weight formulas are
 // the ones stated in include/ubep.h for ubep_gate.
 //
-// One wave per token.  Lane l holds experts l, l + 64, l + 128, ... (each
+// The general kernel (gate_kernel, every shape the call accepts): one wave
+// per token.  Lane l holds experts l, l + 64, l + 128, ... (each
 // load instruction reads 64 consecutive logits).  Groups of a power-of-two
 // size up to 64 are aligned runs of lanes, whose best two logits a butterfly
 // finds; other group sizes go through a copy of the row in LDS, one lane per
 // group.  Every selection decision is an exact fp32 comparison: larger logit
 // first, equal logits to the lower id, made by repeated wave-wide arg-max over
 // (logit, id) pairs.
+#include "device_common.h"
 #include "launch.h"
 
 namespace ubep {
@@ -206,8 +208,216 @@ __global__ __launch_bounds__(kGateThreads) void gate_kernel(GateArgs a) {
     }
 }
 
+// ---------------------------------------------------------------- row kernel
+// Four tokens per wave: token r of a wave owns DPP row r (16 lanes), lane l of
+// the row holds its VPL consecutive logits [l*VPL, (l+1)*VPL) (VPL/4 16-byte
+// loads; a wave reads 4 rows back to back).  A candidate is one 64-bit key:
+// the logit mapped to an order-preserving unsigned word in the high half and
+// the inverted expert id in the low half, so "larger logit first, equal
+// logits to the lower id" is one unsigned comparison and a removed candidate
+// is key 0 (below every finite logit's key).  Each of the k selection rounds
+// is a 4-step rotate-within-row reduction over the lanes' best remaining keys
+// (DPP row_ror 8, 4, 2, 1: after the four steps every lane of the row holds
+// the row's maximum), instead of a wave-wide shuffle butterfly per token; each
+// lane keeps its three best keys, so the lane that wins a round only pops
+// (it rescans its VPL keys below its last pick only after giving all three).
+// Groups: a group spans `span` aligned lanes (gsize = span * VPL); the lanes'
+// top two keys are merged across the span with xor shuffles, and each lane
+// ranks its group's score against the row's G = 16 / span groups.
+constexpr int kRowLanes = 16;
+constexpr int kRowTokensPerWave = 64 / kRowLanes;
+constexpr int kGateRowTokens = kGateThreads / kRowLanes;   // tokens per workgroup
+
+__device__ __forceinline__ uint64_t gate_key(float v, int32_t e) {
+    uint32_t u = __float_as_uint(v);
+    if ((u << 1) == 0u) u = 0u;      // -0 compares equal to +0: one key for both
+    const uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    return ((uint64_t)ord << 32) | (uint32_t)~(uint32_t)e;
+}
+__device__ __forceinline__ float key_value(uint64_t k) {
+    const uint32_t ord = (uint32_t)(k >> 32);
+    return __uint_as_float((ord & 0x80000000u) ? (ord & 0x7FFFFFFFu) : ~ord);
+}
+__device__ __forceinline__ int32_t key_id(uint64_t k) { return (int32_t)~(uint32_t)k; }
+
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t k) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)k, CTRL, 0xF, 0xF, false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(k >> 32), CTRL, 0xF, 0xF, false);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// Every lane of a 16-lane row receives the row's largest key.
+__device__ __forceinline__ uint64_t row_max(uint64_t k) {
+    constexpr int kRowRor = 0x120;   // DPP row_ror:n = 0x120 + n (rotate right within 16 lanes)
+    uint64_t o = dpp_u64<kRowRor + 8>(k);
+    k = o > k ? o : k;
+    o = dpp_u64<kRowRor + 4>(k);
+    k = o > k ? o : k;
+    o = dpp_u64<kRowRor + 2>(k);
+    k = o > k ? o : k;
+    o = dpp_u64<kRowRor + 1>(k);
+    return o > k ? o : k;
+}
+
+// Per-tile counts the gate hands to the layout (ubep_gate_layout): rows per
+// (layout tile, destination rank) and per (layout tile, expert).
+struct GateCounts {
+    int32_t* rank_cnt;       // [n_tiles][R]
+    int32_t* expert_cnt;     // [n_tiles][E]
+    int64_t tile_tokens;     // a multiple of the workgroup's kGateRowTokens tokens
+    int32_t R;
+    uint32_t epr_magic;
+};
+
+template <int VPL, bool COUNT>
+__global__ __launch_bounds__(kGateThreads) void gate_rows_kernel(GateArgs a, int32_t span,
+                                                                 GateCounts gc) {
+    __shared__ int32_t s_rc[COUNT ? kMaxR : 1];
+    __shared__ int32_t s_ec[COUNT ? kGateMaxE : 1];
+    if constexpr (COUNT) {
+        for (int i = threadIdx.x; i < gc.R; i += kGateThreads) s_rc[i] = 0;
+        for (int i = threadIdx.x; i < a.E; i += kGateThreads) s_ec[i] = 0;
+    }
+    const int lane = threadIdx.x & 63;
+    const int rl = lane & (kRowLanes - 1);                  // lane within the token's row
+    const int64_t t = (int64_t)blockIdx.x * kGateRowTokens + (threadIdx.x >> 4);
+    const bool live = t < a.T;
+    const float4* zr = reinterpret_cast<const float4*>(a.logits + (live ? t : 0) * a.E) + rl * (VPL / 4);
+    float4 z4[VPL / 4];
+#pragma unroll
+    for (int i = 0; i < VPL / 4; ++i) z4[i] = zr[i];
+    uint64_t key[VPL];
+#pragma unroll
+    for (int i = 0; i < VPL / 4; ++i) {
+        const int32_t e0 = rl * VPL + 4 * i;
+        key[4 * i] = gate_key(z4[i].x, e0);
+        key[4 * i + 1] = gate_key(z4[i].y, e0 + 1);
+        key[4 * i + 2] = gate_key(z4[i].z, e0 + 2);
+        key[4 * i + 3] = gate_key(z4[i].w, e0 + 3);
+    }
+
+    // the lane's best three keys (its two best also give the group score)
+    uint64_t t1 = 0, t2 = 0, t3 = 0;
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+        const uint64_t k_ = key[i];
+        const bool g1 = k_ > t1, g2 = k_ > t2, g3 = k_ > t3;
+        t3 = g2 ? t2 : (g3 ? k_ : t3);
+        t2 = g1 ? t1 : (g2 ? k_ : t2);
+        t1 = g1 ? k_ : t1;
+    }
+    if (a.groups > 1) {
+        // the group's best two across its span of lanes
+        uint64_t b1 = t1, b2 = t2;
+        for (int o = 1; o < span; o <<= 1) {
+            const uint64_t c1 = __shfl_xor(b1, o, 64), c2 = __shfl_xor(b2, o, 64);
+            const uint64_t hi1 = b1 > c1 ? b1 : c1, lo1 = b1 > c1 ? c1 : b1;
+            const uint64_t hi2 = b2 > c2 ? b2 : c2;
+            b1 = hi1;
+            b2 = lo1 > hi2 ? lo1 : hi2;
+        }
+        const float score = key_value(b1) + key_value(b2);   // one fp32 addition
+        const int32_t G = kRowLanes / span, g = rl / span;
+        const int row0 = lane & ~(kRowLanes - 1);
+        int32_t rank = 0;
+        for (int32_t h = 0; h < G; ++h) {
+            const float sh = __shfl(score, row0 + h * span, 64);
+            rank += (sh > score || (sh == score && h < g)) ? 1 : 0;
+        }
+        if (rank >= a.keep) t1 = t2 = t3 = 0;              // a dropped group offers nothing
+    }
+
+    // k rounds: the row's best remaining key; its owner pops it.  A lane that
+    // has given its three may hold more (below its last pick): when any lane
+    // of the wave is in that state, those lanes rescan for their next three.
+    bool more = t3 != 0;          // this lane may hold candidates past t3
+    uint64_t last = 0;            // this lane's last pick
+    uint64_t mine = 0, top = 0;
+    for (int32_t j = 0; j < a.k; ++j) {
+        const uint64_t best = row_max(t1);
+        if (j == 0) top = best;
+        if (rl == j) mine = best;
+        if (t1 == best && best != 0) {
+            last = best;
+            t1 = t2;
+            t2 = t3;
+            t3 = 0;
+        }
+        const bool refill = more && t1 == 0;
+        if (__any(refill)) {
+            if (refill) {
+#pragma unroll
+                for (int i = 0; i < VPL; ++i) {
+                    const uint64_t k_ = key[i] < last ? key[i] : 0ull;
+                    const bool g1 = k_ > t1, g2 = k_ > t2, g3 = k_ > t3;
+                    t3 = g2 ? t2 : (g3 ? k_ : t3);
+                    t2 = g1 ? t1 : (g2 ? k_ : t2);
+                    t1 = g1 ? k_ : t1;
+                }
+                more = t3 != 0;
+            }
+        }
+    }
+
+    // weights over the selected experts, in fp32; the row's sum from its lane 0
+    const bool sel = rl < a.k;
+    const float mv = key_value(mine), tv = key_value(top);
+    float u = 0.0f;
+    if (sel) u = a.norm == UBEP_GATE_SOFTMAX ? expf(mv - tv) : 1.0f / (1.0f + expf(-mv));
+    float sum = u;
+    for (int o = 1; o < kRowLanes; o <<= 1) sum += __shfl_xor(sum, o, 64);
+    sum = __shfl(sum, lane & ~(kRowLanes - 1), 64);
+    if (live && sel) {
+        a.idx[t * a.k + rl] = key_id(mine);
+        a.w[t * a.k + rl] = u / sum;
+    }
+    if constexpr (COUNT) {
+        // this workgroup's tokens all lie in one layout tile: count its rows
+        // per rank and per expert in LDS, then add the nonzero counts to the
+        // tile's rows of the workspace arrays
+        __syncthreads();
+        if (live && sel) {
+            const uint32_t e = (uint32_t)key_id(mine);
+            atomicAdd(&s_rc[rank_of(e, gc.epr_magic)], 1);
+            atomicAdd(&s_ec[e], 1);
+        }
+        __syncthreads();
+        const int64_t tile = (int64_t)blockIdx.x * kGateRowTokens / gc.tile_tokens;
+        for (int i = threadIdx.x; i < gc.R; i += kGateThreads)
+            if (s_rc[i] != 0) add_relaxed(reinterpret_cast<uint32_t*>(gc.rank_cnt + tile * gc.R + i), (uint32_t)s_rc[i]);
+        for (int i = threadIdx.x; i < a.E; i += kGateThreads)
+            if (s_ec[i] != 0) add_relaxed(reinterpret_cast<uint32_t*>(gc.expert_cnt + tile * a.E + i), (uint32_t)s_ec[i]);
+    }
+}
+
+// The row kernel covers E = 16 * VPL with VPL in {4, 8, 16} (E in {64, 128,
+// 256}), k <= 16, 16-byte aligned logits, and groups that are aligned
+// power-of-two runs of whole lanes.
+static int gate_row_vpl(const ubep_gate_shape& g, const float* logits) {
+    if (g.k > kRowLanes || ((uintptr_t)logits % 16) != 0) return 0;
+    if (g.E != 64 && g.E != 128 && g.E != 256) return 0;
+    const int vpl = g.E / kRowLanes;
+    if (g.groups > 1) {
+        const int gsize = g.E / g.groups;
+        if (gsize % vpl != 0) return 0;
+        const int span = gsize / vpl;
+        if ((span & (span - 1)) != 0 || span > kRowLanes) return 0;
+    }
+    return vpl;
+}
+
 hipError_t launch_gate(const ubep_gate_shape& g, const float* logits, int32_t* idx, float* w,
                        hipStream_t stream) {
+    return launch_gate_counting(g, logits, idx, w, nullptr, stream);
+}
+
+bool gate_counts_fit(const ubep_gate_shape& g, const float* logits, int64_t tile_tokens) {
+    return gate_row_vpl(g, logits) != 0 && tile_tokens % kGateRowTokens == 0;
+}
+
+hipError_t launch_gate_counting(const ubep_gate_shape& g, const float* logits, int32_t* idx,
+                                float* w, const GateCountArgs* counts, hipStream_t stream) {
     GateArgs a;
     a.logits = logits;
     a.idx = idx;
@@ -218,6 +428,27 @@ hipError_t launch_gate(const ubep_gate_shape& g, const float* logits, int32_t* i
     a.groups = g.groups;
     a.keep = g.keep_groups;
     a.norm = g.norm;
+    const int rv = gate_row_vpl(g, logits);
+    if (counts != nullptr && (rv == 0 || counts->tile_tokens % kGateRowTokens != 0))
+        return hipErrorInvalidValue;                 // callers check gate_counts_fit first
+    if (rv != 0) {
+        const int32_t span = g.groups > 1 ? (g.E / g.groups) / rv : 1;
+        const dim3 grid((unsigned)((g.T + kGateRowTokens - 1) / kGateRowTokens)), block(kGateThreads);
+        GateCounts gc{};
+        if (counts != nullptr) {
+            gc.rank_cnt = counts->rank_cnt;
+            gc.expert_cnt = counts->expert_cnt;
+            gc.tile_tokens = counts->tile_tokens;
+            gc.R = counts->R;
+            gc.epr_magic = counts->epr_magic;
+            if (rv == 4) return launch_kernel(gate_rows_kernel<4, true>, grid, block, 0, stream, a, span, gc);
+            if (rv == 8) return launch_kernel(gate_rows_kernel<8, true>, grid, block, 0, stream, a, span, gc);
+            return launch_kernel(gate_rows_kernel<16, true>, grid, block, 0, stream, a, span, gc);
+        }
+        if (rv == 4) return launch_kernel(gate_rows_kernel<4, false>, grid, block, 0, stream, a, span, gc);
+        if (rv == 8) return launch_kernel(gate_rows_kernel<8, false>, grid, block, 0, stream, a, span, gc);
+        return launch_kernel(gate_rows_kernel<16, false>, grid, block, 0, stream, a, span, gc);
+    }
     const int64_t blocks = (g.T + kGateWaves - 1) / kGateWaves;
     const int vpl = (g.E + 63) / 64;
     if (vpl <= 1) return launch_kernel(gate_kernel<1>, dim3((unsigned)blocks), dim3(kGateThreads), 0, stream, a);

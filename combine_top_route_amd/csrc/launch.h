@@ -83,6 +83,26 @@ hipError_t launch_chunk_lpt(const Plan& p, const int32_t* chunk_offset, const in
 hipError_t launch_gate(const ubep_gate_shape& g, const float* logits, int32_t* idx, float* w,
                        hipStream_t stream);
 
+// The gate that also counts its selections per layout tile (ubep_gate_layout).
+struct GateCountArgs {
+    int32_t* rank_cnt;       // [n_tiles][R], zero on entry
+    int32_t* expert_cnt;     // [n_tiles][E], zero on entry
+    int64_t tile_tokens;
+    int32_t R;
+    uint32_t epr_magic;
+};
+bool gate_counts_fit(const ubep_gate_shape& g, const float* logits, int64_t tile_tokens);
+hipError_t launch_gate_counting(const ubep_gate_shape& g, const float* logits, int32_t* idx,
+                                float* w, const GateCountArgs* counts, hipStream_t stream);
+
+// The layout from per-tile counts that the counting gate left in the workspace.
+hipError_t launch_layout_from_counts(const Plan& p, const int32_t* idx, int32_t* pos,
+                                     int32_t* expert_count, int32_t* rank_count,
+                                     int32_t* recv_offset, int32_t* send_offset,
+                                     int32_t* chunk_offset, int32_t* recv_src, void* ws,
+                                     hipStream_t stream);
+bool layout_from_counts_fits(const Plan& p);
+
 hipError_t launch_sentinel_pipeline(const Plan& p, const void* x, const int32_t* pos,
                                     const float* topk_w, void* recv, void* out, uint64_t spin_ticks,
                                     uint32_t debug_flags, void* ws, int device, hipStream_t stream);

@@ -408,6 +408,166 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_replicated_kernel(Layou
     if (bad_pos) raise_status(a.status, UBEP_ERR_BAD_POSITION);
 }
 
+// ---------------------------------------------------------------- layout from gate counts
+// The second half of ubep_gate_layout: the gate has already counted its
+// selections per (tile, rank) and per (tile, expert) into the workspace, so a
+// workgroup per tile needs no sweep of the ids and no word from another
+// workgroup of this kernel: one round of loads of the counts gives its tile's
+// exclusive prefixes and the totals, and it ranks its own tile as the other
+// layouts do.  The last workgroup to finish clears the counts for the next
+// call (the workspace starts zero-filled).
+bool layout_from_counts_fits(const Plan& p) {
+    const int64_t e_per = (p.E + p.n_tiles - 1) / p.n_tiles;
+    return p.R <= kRepMaxK && e_per <= kRepMaxSlice && p.n_tiles <= 65535;
+}
+
+template <int LR>
+__global__ __launch_bounds__(kLayoutThreads) void layout_counts_kernel(LayoutArgs a,
+                                                                       int32_t* rank_cnt,
+                                                                       int32_t* expert_cnt) {
+    __shared__ int32_t s_before[kRepMaxK];     // rows to rank d in earlier tiles
+    __shared__ int32_t s_total[kRepMaxK];      // rows to rank d
+    __shared__ int32_t s_off[kRepMaxK];        // exclusive scan of the totals
+    __shared__ int32_t s_wh[kLayoutWaves * kRepMaxK];
+    __shared__ int32_t s_eh[kRepMaxSlice];
+    __shared__ int32_t s_tmp[kLayoutWaves];
+    constexpr int T_ = kLayoutThreads;
+    const Plan& p = a.p;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int64_t tile = blockIdx.x;
+    const int32_t R = p.R, E = p.E;
+    const int32_t n_tiles = (int32_t)p.n_tiles;
+    const int32_t e_per = (E + n_tiles - 1) / n_tiles;
+    const int32_t e_lo = (int64_t)tile * e_per < E ? (int32_t)tile * e_per : E;
+    const int32_t n_e = E - e_lo < e_per ? E - e_lo : e_per;
+
+    int32_t ev[LR];
+    load_ids<kLayoutWaves, LR>(a, tile, ev);
+    for (int i = tid; i < R; i += T_) s_before[i] = s_total[i] = 0;
+    for (int i = tid; i < kLayoutWaves * R; i += T_) s_wh[i] = 0;
+    for (int i = tid; i < n_e; i += T_) s_eh[i] = 0;
+    __syncthreads();
+    // every tile's rank counts and this workgroup's slice of expert counts
+    const int64_t nr = (int64_t)n_tiles * R;
+    for (int64_t i = tid; i < nr; i += T_) {
+        const int32_t tau = (int32_t)(i / R), d = (int32_t)(i - (int64_t)tau * R);
+        const int32_t c = rank_cnt[i];
+        atomicAdd(&s_total[d], c);
+        if (tau < tile) atomicAdd(&s_before[d], c);
+    }
+    const int64_t ne = (int64_t)n_tiles * n_e;
+    for (int64_t i = tid; i < ne; i += T_) {
+        const int32_t tau = (int32_t)(i / n_e), e = (int32_t)(i - (int64_t)tau * n_e);
+        atomicAdd(&s_eh[e], expert_cnt[(int64_t)tau * E + e_lo + e]);
+    }
+    bool bad = false, bad_pos = false;
+    check_ids<kLayoutWaves, LR>(p, ev, &bad);
+    {
+        int64_t lo, hi;
+        wave_rows<kLayoutWaves>(p, w, &lo, &hi);
+#pragma unroll
+        for (int i = 0; i < LR; ++i)
+            if (lo + 64 * i + lane < hi) atomicAdd(&s_wh[w * R + (int32_t)rank_of((uint32_t)ev[i], p.epr_magic)], 1);
+    }
+    __syncthreads();
+    // every count has been read: count this workgroup out; the last one
+    // clears the counts for the next call
+    if (tid == 0) {
+        const uint32_t done = add_relaxed(&a.hdr[kHdrGateLayoutDone], 1u);
+        s_tmp[0] = done == gridDim.x - 1u ? 1 : 0;
+    }
+    __syncthreads();
+    if (s_tmp[0] != 0) {
+        for (int64_t i = tid; i < nr; i += T_) rank_cnt[i] = 0;
+        for (int64_t i = tid; i < (int64_t)n_tiles * E; i += T_) expert_cnt[i] = 0;
+        if (tid == 0) st_relaxed(&a.hdr[kHdrGateLayoutDone], 0u);
+    }
+    __syncthreads();
+    {   // exclusive scan of the rank totals; thread i owns a run of ranks
+        const int per = (R + T_ - 1) / T_;
+        int32_t mine = 0;
+        for (int i = 0; i < per; ++i) {
+            const int32_t d = tid * per + i;
+            if (d < R) mine += s_total[d];
+        }
+        int32_t inc = mine;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int32_t u = __shfl_up(inc, o, 64);
+            if (lane >= o) inc += u;
+        }
+        if (lane == 63) s_tmp[w] = inc;
+        __syncthreads();
+        int32_t run = inc - mine;
+        for (int i = 0; i < w; ++i) run += s_tmp[i];
+        for (int i = 0; i < per; ++i) {
+            const int32_t d = tid * per + i;
+            if (d < R) {
+                s_off[d] = run;
+                run += s_total[d];
+            }
+        }
+    }
+    __syncthreads();
+    for (int32_t d = tid; d < R; d += T_) {
+        int32_t run = s_off[d] + s_before[d];
+#pragma unroll
+        for (int v_ = 0; v_ < kLayoutWaves; ++v_) {
+            const int32_t c = s_wh[v_ * R + d];
+            s_wh[v_ * R + d] = run;
+            run += c;
+        }
+    }
+    __syncthreads();
+    int32_t q[LR];
+    tile_ranks<kLayoutWaves, LR, false>(p, ev, s_wh, q);
+    store_positions<kLayoutWaves, LR, false>(a, tile, q, &bad_pos);
+    const int64_t tok0 = tile * p.tile_tokens;
+    if (tok0 % p.tps == 0)
+        for (int32_t d = tid; d < R; d += T_) a.send_offset[(tok0 / p.tps) * R + d] = s_before[d];
+    if (a.chunk_offset != nullptr && tok0 % p.tpc == 0)
+        for (int32_t d = tid; d < R; d += T_) a.chunk_offset[(tok0 / p.tpc) * R + d] = s_before[d];
+    for (int i = tid; i < n_e; i += T_) a.expert_count[e_lo + i] = s_eh[i];
+    if (tile == 0) {
+        for (int32_t d = tid; d < R; d += T_) {
+            a.rank_count[d] = s_total[d];
+            a.recv_offset[d] = s_off[d];
+        }
+        if (tid == 0) a.recv_offset[R] = (int32_t)p.rows;
+    }
+    if (bad) raise_status(a.status, UBEP_ERR_BAD_EXPERT_ID);
+    if (bad_pos) raise_status(a.status, UBEP_ERR_BAD_POSITION);
+}
+
+hipError_t launch_layout_from_counts(const Plan& p, const int32_t* idx, int32_t* pos,
+                                     int32_t* expert_count, int32_t* rank_count,
+                                     int32_t* recv_offset, int32_t* send_offset,
+                                     int32_t* chunk_offset, int32_t* recv_src, void* ws,
+                                     hipStream_t stream) {
+    LayoutArgs a{};
+    a.idx = idx;
+    a.pos = pos;
+    a.expert_count = expert_count;
+    a.rank_count = rank_count;
+    a.recv_offset = recv_offset;
+    a.send_offset = send_offset;
+    a.chunk_offset = p.C > 1 ? chunk_offset : nullptr;
+    a.recv_src = recv_src;
+    a.expert_offset = nullptr;
+    char* base = static_cast<char*>(ws);
+    a.hdr = reinterpret_cast<uint32_t*>(base);
+    a.p = p;
+    a.status = a.hdr + kHdrStatus;
+    int32_t* rc = reinterpret_cast<int32_t*>(base + p.off_gate_rank);
+    int32_t* ec = reinterpret_cast<int32_t*>(base + p.off_gate_expert);
+    const int64_t lane_rows = (p.tile_rows + kLayoutThreads - 1) / kLayoutThreads;
+    const dim3 g((unsigned)p.n_tiles), b(kLayoutThreads);
+    if (lane_rows <= 1) return launch_kernel(layout_counts_kernel<1>, g, b, 0, stream, a, rc, ec);
+    if (lane_rows <= 2) return launch_kernel(layout_counts_kernel<2>, g, b, 0, stream, a, rc, ec);
+    if (lane_rows <= 4) return launch_kernel(layout_counts_kernel<4>, g, b, 0, stream, a, rc, ec);
+    return launch_kernel(layout_counts_kernel<8>, g, b, 0, stream, a, rc, ec);
+}
+
 // ---------------------------------------------------------------- allocation-free layout
 // The workspace of ubep_layout_noalloc: one array per device for the life of
 // the process, shared by every such call on that device.  Host code never

@@ -41,6 +41,7 @@ constexpr int kHdrSentTicket = 352;    // task ticket of the sentinel-readiness 
 constexpr int kHdrSentDone = 384;      // workgroups finished in the sentinel-readiness pipeline
 constexpr int kHdrSentGiveUp = 416;    // set once a sentinel wait has expired: later waits give up
 constexpr int kHdrFusedGiveUp = 448;   // set once a chunk-flag wait has expired: later waits give up
+constexpr int kHdrGateLayoutDone = 480; // workgroups finished in the layout from gate counts
 constexpr size_t kHdrBytes = 2048;
 // Readiness sentinel of the sentinel-polling pipeline: every 32-bit word of a
 // receive row's first 16-byte unit while the row is empty (two bf16 NaNs).
@@ -90,6 +91,8 @@ struct Plan {
     size_t off_flags;      // uint32 [C][kFlagStride] chunk ready flags
     size_t ws_bytes;
     size_t off_order;      // int32  [C] chunk order computed on the device (LPT policy)
+    size_t off_gate_rank;  // int32  [n_tiles][R] rows per (tile, rank) counted by the gate
+    size_t off_gate_expert; // int32 [n_tiles][E] rows per (tile, expert) counted by the gate
     // Position keys (last, so that the fields the rank-order kernels read keep
     // their places).  Rank order: rows sort by (rank, token, slot), one key
     // per rank.  Expert order: rows sort by (expert, token, slot), one key per

@@ -230,6 +230,25 @@ typedef struct {
 ubep_status ubep_gate(const ubep_gate_shape *gate /*host*/, const float *logits,
                       int32_t *topk_idx, float *topk_w, hipStream_t stream);
 
+/* The gate and the dispatch layout with the selection feeding the layout's
+ * counts (the gate's selections are the layout's "token counting", "Kernel
+ * Decomposition" section, and each token goes to the experts its gate selects,
+ * opening section).  Outputs are exactly those of ubep_gate(gate, logits,
+ * topk_idx, topk_w) followed by ubep_layout(shape, topk_idx, pos, ...) on the
+ * same stream.  gate->T, E, k must equal shape->T, E, k.  Two kernels on
+ * `stream`: the gate also counts its selections per layout tile and per
+ * destination rank and expert into the workspace, and the layout then reads
+ * those counts instead of sweeping the ids or waiting on other workgroups
+ * (one workgroup per tile; the last one clears the counts).  Shapes outside
+ * that pair (gate shapes other than E in {64, 128, 256} with k <= 16 and
+ * groups of whole aligned lane runs, 16-byte aligned logits, layout tiles of
+ * a multiple of 16 tokens, R <= 1024) run as the two separate calls. */
+ubep_status ubep_gate_layout(const ubep_gate_shape *gate /*host*/, const ubep_shape *shape /*host*/,
+                             const float *logits, int32_t *topk_idx, float *topk_w, int32_t *pos,
+                             int32_t *expert_count, int32_t *rank_count, int32_t *recv_offset,
+                             int32_t *send_offset, int32_t *chunk_offset, int32_t *recv_src,
+                             void *ws, size_t ws_bytes, hipStream_t stream);
+
 /* Dispatch ("send tokens" + "reorder tokens", written straight into the final
  * receive row: no relay buffer).  For every (t, j):
  *   UBEP_BF16:     recv[pos[t][j]][:] = x[t][:]           (bf16 [T*k][H], bit copy)
