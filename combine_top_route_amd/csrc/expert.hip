@@ -38,7 +38,8 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kGemmThreads = 256;
 constexpr int kBN = 128;                 // output channels per tile
-constexpr int kBM = 128;                 // rows per tile
+constexpr int kBShort = 128;             // rows per tile of experts with at most this many rows
+constexpr int kBTall = 192;              // rows per tile of the others
 constexpr int kBK = 64;                  // channels per k step
 constexpr int kLdsStride = kBK;          // bf16 per LDS row: 128 bytes, 16-byte units swizzled
 static_assert(kBK == 64, "the LDS swizzle permutes the 8 units of a 64-channel row");
@@ -51,7 +52,8 @@ __device__ __forceinline__ int lds_at(int r, int u) { return r * kLdsStride + ((
 constexpr int kPerThreadE = kExpertMaxE / kGemmThreads;
 constexpr int kVecPerRow = kBK / 8;                          // 16-byte vectors per tile row
 constexpr int kLoadsW = kBN * kVecPerRow / kGemmThreads;     // weight vectors per thread and step
-constexpr int kLoadsX = kBM * kVecPerRow / kGemmThreads;     // receive-row vectors per thread and step
+template <int BM>
+constexpr int loads_x() { return BM * kVecPerRow / kGemmThreads; }   // receive-row vectors per thread and step
 
 struct ExpertArgs {
     const int32_t* eoff;     // [E+1]
@@ -61,6 +63,7 @@ struct ExpertArgs {
     uint32_t* status;
     int64_t H, N, n_rows;
     int32_t E;
+    int32_t rows_class;      // 0: every expert; 1: experts of at most kBShort rows; 2: the others
 };
 
 __device__ __forceinline__ uint2 pack_bf16x4(f32x4 v) {
@@ -70,9 +73,13 @@ __device__ __forceinline__ uint2 pack_bf16x4(f32x4 v) {
     return o;
 }
 
+template <int BM>
 __global__ __launch_bounds__(kGemmThreads, 2) void expert_linear_kernel(ExpertArgs a) {
+    constexpr int kBM = BM;
+    constexpr int kLoadsX = loads_x<BM>();
+    constexpr int JT = BM / 32;                          // 16-row MFMA tiles per wave (two waves share the rows)
     __shared__ __attribute__((aligned(16))) uint16_t s_w[kBN * kLdsStride];
-    __shared__ __attribute__((aligned(16))) uint16_t s_x[kBM * kLdsStride];
+    __shared__ __attribute__((aligned(16))) uint16_t s_x[BM * kLdsStride];
     __shared__ int32_t s_wsum[kGemmThreads / 64];
     __shared__ int32_t s_sel[2];
 
@@ -95,12 +102,14 @@ __global__ __launch_bounds__(kGemmThreads, 2) void expert_linear_kernel(ExpertAr
             const int32_t lo = a.eoff[e], hi = a.eoff[e + 1];
             const int32_t rows = hi - lo;
             if (rows < 0 || lo < 0 || (int64_t)hi > a.n_rows || (e == 0 && lo != 0)) bad_off = true;
-            c = rows > 0 ? (rows + kBM - 1) / kBM : 0;
+            const bool in_class = a.rows_class == 0 || (a.rows_class == 1) == (rows <= kBShort);
+            c = rows > 0 && in_class ? (rows + kBM - 1) / kBM : 0;
         }
         cnt[i] = c;
         mine += c;
     }
-    if (bad_off && blockIdx.x == 0 && blockIdx.y == 0) raise_status(a.status, UBEP_ERR_BAD_POSITION);
+    if (bad_off && blockIdx.x == 0 && blockIdx.y == 0 && a.rows_class <= 1)
+        raise_status(a.status, UBEP_ERR_BAD_POSITION);
     int32_t inc = mine;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
@@ -175,27 +184,28 @@ __global__ __launch_bounds__(kGemmThreads, 2) void expert_linear_kernel(ExpertAr
         }
         __syncthreads();
     };
-    f32x4 acc[4][4];
+    f32x4 acc[4][JT];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int j = 0; j < JT; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-    const int wn = (wave & 1) * 64, wm = (wave >> 1) * 64;
+    const int wn = (wave & 1) * 64, wm = (wave >> 1) * (BM / 2);
     const int fr = lane & 15, fk = (lane >> 4) * 8;      // fragment row and channel offset
     auto multiply = [&]() {
 #pragma unroll
         for (int ks = 0; ks < kBK; ks += 32) {
-            bf16x8 fa[4], fb[4];
+            bf16x8 fa[4], fb[JT];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
+            for (int i = 0; i < 4; ++i)
                 fa[i] = *reinterpret_cast<const bf16x8*>(&s_w[lds_at(wn + 16 * i + fr, (ks + fk) >> 3)]);
-                fb[i] = *reinterpret_cast<const bf16x8*>(&s_x[lds_at(wm + 16 * i + fr, (ks + fk) >> 3)]);
-            }
+#pragma unroll
+            for (int j = 0; j < JT; ++j)
+                fb[j] = *reinterpret_cast<const bf16x8*>(&s_x[lds_at(wm + 16 * j + fr, (ks + fk) >> 3)]);
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
+                for (int j = 0; j < JT; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
         }
     };
@@ -215,7 +225,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void expert_linear_kernel(ExpertAr
     // ---- epilogue: lane holds channels n .. n+3 of row r for each (i, j)
     const int64_t nq = a.N / 4;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < JT; ++j) {
         const int64_t r = r_lo + wm + 16 * j + fr;
         if (r >= r_end) continue;
 #pragma unroll
@@ -264,10 +274,24 @@ hipError_t launch_expert_linear(int32_t E, int64_t H, int64_t N, int64_t n_rows,
     a.N = N;
     a.n_rows = n_rows;
     a.E = E;
-    // row tiles over all experts: at most ceil(n_rows / 128) + E (one partial tile each)
-    const int64_t row_tiles = (n_rows + kBM - 1) / kBM + E;
-    return launch_kernel(expert_linear_kernel, dim3((unsigned)(N / kBN), (unsigned)row_tiles),
-                         dim3(kGemmThreads), 0, stream, a);
+    // Two launches by expert size: an expert whose rows need two tiles
+    // streams its weights twice, so experts of more than 128 rows (about half
+    // of them in a decode step of 128 rows per expert) take 192-row tiles,
+    // while the others keep 128-row tiles and multiply no more zero rows than
+    // they must.  The pending timing pair spans both launches.
+    const LaunchEvents ev = take_launch_events();
+    const dim3 block(kGemmThreads);
+    a.rows_class = 1;                                 // at most one 128-row tile per expert
+    hipError_t e = launch_kernel_ev(expert_linear_kernel<kBShort>, dim3((unsigned)(N / kBN), (unsigned)E),
+                                    block, 0, stream, ev.start, nullptr, a);
+    if (e != hipSuccess) return e;
+    // experts above 128 rows: at most n_rows / 129 of them, each with one partial tile
+    const int64_t tall_e = n_rows / (kBShort + 1) < E ? n_rows / (kBShort + 1) : E;
+    const int64_t tall_tiles = (n_rows + kBTall - 1) / kBTall + tall_e;
+    a.rows_class = 2;
+    return launch_kernel_ev(expert_linear_kernel<kBTall>,
+                            dim3((unsigned)(N / kBN), (unsigned)(tall_tiles > 0 ? tall_tiles : 1)),
+                            block, 0, stream, nullptr, ev.stop, a);
 }
 
 }  // namespace ubep

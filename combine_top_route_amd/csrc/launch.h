@@ -24,9 +24,11 @@ LaunchEvents take_launch_events();
 // Every library kernel launches through here: the arguments are converted to
 // the kernel's parameter types, and a pending event pair is recorded by the
 // dispatch itself (hipExtLaunchKernel), with no marker packet in the stream.
+// launch_kernel with explicit events (each may be null): a call of several
+// launches hands its pending pair out across them.
 template <typename... P, typename... A>
-hipError_t launch_kernel(void (*kernel)(P...), dim3 grid, dim3 block, size_t lds, hipStream_t stream,
-                         A... args) {
+hipError_t launch_kernel_ev(void (*kernel)(P...), dim3 grid, dim3 block, size_t lds, hipStream_t stream,
+                            hipEvent_t start, hipEvent_t stop, A... args) {
     static_assert(sizeof...(P) == sizeof...(A), "kernel argument count");
     std::tuple<P...> vals{static_cast<P>(args)...};
     void* ptrs[sizeof...(P) > 0 ? sizeof...(P) : 1];
@@ -34,9 +36,15 @@ hipError_t launch_kernel(void (*kernel)(P...), dim3 grid, dim3 block, size_t lds
         int i = 0;
         ((ptrs[i++] = static_cast<void*>(&v)), ...);
     }, vals);
-    const LaunchEvents ev = take_launch_events();
     return hipExtLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, ptrs, lds, stream,
-                              ev.start, ev.stop, 0);
+                              start, stop, 0);
+}
+
+template <typename... P, typename... A>
+hipError_t launch_kernel(void (*kernel)(P...), dim3 grid, dim3 block, size_t lds, hipStream_t stream,
+                         A... args) {
+    const LaunchEvents ev = take_launch_events();
+    return launch_kernel_ev(kernel, grid, block, lds, stream, ev.start, ev.stop, args...);
 }
 
 // expert_offset: [E+1] output of the expert order (p.order == 1), may be null.
