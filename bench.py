@@ -68,6 +68,7 @@ KERNEL_SOURCES = {
     "combine": ["combine.hip", "rows.h", "launch.h", "device_common.h", "plan.h"],
     "dispatch": ["dispatch.hip", "rows.h", "launch.h", "device_common.h", "plan.h"],
     "layout": ["layout.hip", "layout_worker.h", "launch.h", "device_common.h", "plan.h"],
+    "expert": ["expert.hip", "rows.h", "launch.h", "device_common.h", "plan.h"],
 }
 
 
