@@ -232,35 +232,34 @@ int64_t layout_workers(const Plan& p, int cus) {
 // ---------------------------------------------------------------- replicated layout
 // Small problems with several tiles (up to kRepMaxRows rows, e.g. a
 // 4096-token decode step of 32768 rows): every workgroup owns one tile and
-// sweeps ALL the ids itself (a few hundred KB, read from L2), counting per key
-// the rows before its tile and the rest.  That gives its tile's exclusive
-// prefixes and the key totals with no value crossing workgroups: no tickets,
+// sweeps ALL the ids itself (a few hundred KB, read from L2), counting per
+// expert the rows before its tile and the rest (per-rank counts are sums over
+// the rank's experts).  That gives its tile's exclusive prefixes and the key
+// totals with no value crossing workgroups: no tickets,
 // no published words, no polling -- the round trips through device memory
 // that bound the persistent kernel at this size -- at the price of the ids
 // being read once per workgroup.  Then it ranks its own tile as the
 // persistent kernel does (per-wave counts, ballot peer masks).  Under skewed
-// routing many lanes of one atomic hit the same hot key and serialise, so
-// for up to 256 keys the counts go to four copies (by lane), summed after.
+// routing many lanes of one atomic hit the same hot expert and serialise, so
+// for up to 256 experts the counts go to four copies (by lane), summed after.
 constexpr int64_t kRepMaxRows = 32768;
 constexpr int kRepMaxK = 1024;
 constexpr int kRepMaxSlice = 1024;
 constexpr int kRepMaxTiles = 256;
 
 bool layout_replicates(const Plan& p, const int32_t* idx) {
-    const int32_t K = p.order ? p.E : p.R;
-    const int64_t e_per = (p.E + p.n_tiles - 1) / p.n_tiles;
     return g_worker_cap_default() && p.rows <= kRepMaxRows && p.rows % 4 == 0 &&
            ((uintptr_t)idx % 16) == 0 && p.n_tiles >= 2 && p.n_tiles <= kRepMaxTiles &&
-           K <= kRepMaxK && e_per <= kRepMaxSlice;
+           p.E <= kRepMaxK;                              // the sweep's keys are experts (E >= R)
 }
 
 template <int LR, int NV, bool EORD>
 __global__ __launch_bounds__(kLayoutThreads) void layout_replicated_kernel(LayoutArgs a) {
-    // [copy][0][q]: rows with key q before this tile; [copy][1][q]: the others
+    // [copy][0][e]: rows to expert e before this tile; [copy][1][e]: the others
     __shared__ int32_t s_hist[2 * kRepMaxK];
+    __shared__ int32_t s_rk[2 * kRepMaxK];         // rank order: the same two halves per rank
     __shared__ int32_t s_off[kRepMaxK];            // exclusive scan of the key totals
     __shared__ int32_t s_wh[kLayoutWaves * kRepMaxK];   // this tile's per-wave key counts, then row bases
-    __shared__ int32_t s_eh[kRepMaxSlice];         // expert counts of this workgroup's slice (rank order)
     __shared__ int32_t s_tmp[kLayoutWaves];
     constexpr int T_ = kLayoutThreads;
     const Plan& p = a.p;
@@ -268,12 +267,9 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_replicated_kernel(Layou
     const int64_t tile = blockIdx.x;
     const int64_t t_start = tile * p.tile_rows;
     const int32_t R = p.R, E = p.E, epr = p.epr;
-    const int32_t K = EORD ? E : R;
-    const int32_t e_per = (E + (int32_t)gridDim.x - 1) / (int32_t)gridDim.x;
-    const int32_t e_lo = (int64_t)tile * e_per < E ? (int32_t)tile * e_per : E;
-    const int32_t n_e = EORD ? 0 : (E - e_lo < e_per ? E - e_lo : e_per);
-    const int32_t copies = K <= kRepMaxK / 4 ? 4 : 1;    // both fit s_hist
-    const int32_t my_copy = (tid & (copies - 1)) * 2 * K;
+    const int32_t K = EORD ? E : R;                        // the layout's keys
+    const int32_t copies = E <= kRepMaxK / 4 ? 4 : 1;      // both fit s_hist
+    const int32_t my_copy = (tid & (copies - 1)) * 2 * E;
 
     // this tile's ids first, then the sweep over every row (int4 loads, all in
     // flight together; clamped, so every address is valid)
@@ -287,25 +283,34 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_replicated_kernel(Layou
         const int64_t i = tid + (int64_t)j * T_;
         v[j] = src[i < n4 ? i : n4 - 1];
     }
-    for (int i = tid; i < 2 * K * copies; i += T_) s_hist[i] = 0;
+    for (int i = tid; i < 2 * E * copies; i += T_) s_hist[i] = 0;
     for (int i = tid; i < kLayoutWaves * K; i += T_) s_wh[i] = 0;
-    for (int i = tid; i < n_e; i += T_) s_eh[i] = 0;
     __syncthreads();
 
-    const auto count_row = [&](int64_t row, int32_t e) {
-        if ((uint32_t)e >= (uint32_t)E) e = 0;            // as the other modes: expert 0 (reported below)
-        const uint32_t q = EORD ? (uint32_t)e : rank_of((uint32_t)e, p.epr_magic);
-        atomicAdd(&s_hist[my_copy + (row < t_start ? 0 : K) + (int32_t)q], 1);
-        if (!EORD && (uint32_t)(e - e_lo) < (uint32_t)n_e) atomicAdd(&s_eh[e - e_lo], 1);
+    // The sweep counts experts, one LDS atomic per row; a rank's counts are
+    // the sums over its experts, taken once afterwards.  Ids outside [0, E)
+    // count as expert 0, as in the other modes (reported below).
+    const auto count = [&](int32_t* h, int32_t e) {
+        atomicAdd(&h[(uint32_t)e < (uint32_t)E ? e : 0], 1);
     };
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
         const int64_t i = tid + (int64_t)j * T_;
         if (i < n4) {
-            count_row(4 * i, v[j].x);
-            count_row(4 * i + 1, v[j].y);
-            count_row(4 * i + 2, v[j].z);
-            count_row(4 * i + 3, v[j].w);
+            const int64_t r0 = 4 * i;
+            int32_t* h = s_hist + my_copy + (r0 < t_start ? 0 : E);
+            if (r0 < t_start && r0 + 4 > t_start) {          // the one vector astride the tile start
+                int32_t* g = s_hist + my_copy + E;
+                count(r0 + 0 < t_start ? h : g, v[j].x);
+                count(r0 + 1 < t_start ? h : g, v[j].y);
+                count(r0 + 2 < t_start ? h : g, v[j].z);
+                count(r0 + 3 < t_start ? h : g, v[j].w);
+            } else {
+                count(h, v[j].x);
+                count(h, v[j].y);
+                count(h, v[j].z);
+                count(h, v[j].w);
+            }
         }
     }
     // this tile's per-wave key counts
@@ -324,9 +329,21 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_replicated_kernel(Layou
     }
     __syncthreads();
     if (copies > 1) {
-        for (int i = tid; i < 2 * K; i += T_)
-            s_hist[i] += s_hist[2 * K + i] + s_hist[4 * K + i] + s_hist[6 * K + i];
+        for (int i = tid; i < 2 * E; i += T_)
+            s_hist[i] += s_hist[2 * E + i] + s_hist[4 * E + i] + s_hist[6 * E + i];
         __syncthreads();
+    }
+    // kh[q]: rows with key q before this tile; kh[K + q]: the others
+    const int32_t* kh = s_hist;
+    if (!EORD) {
+        for (int i = tid; i < 2 * R; i += T_) {
+            const int32_t half = i < R ? 0 : E, d = i < R ? i : i - R;
+            int32_t c = 0;
+            for (int32_t e = d * epr; e < (d + 1) * epr; ++e) c += s_hist[half + e];
+            s_rk[i] = c;
+        }
+        __syncthreads();
+        kh = s_rk;
     }
 
     {   // exclusive scan of the key totals; thread i owns a run of keys
@@ -334,7 +351,7 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_replicated_kernel(Layou
         int32_t mine = 0;
         for (int i = 0; i < per; ++i) {
             const int32_t d = tid * per + i;
-            if (d < K) mine += s_hist[d] + s_hist[K + d];
+            if (d < K) mine += kh[d] + kh[K + d];
         }
         int32_t inc = mine;
 #pragma unroll
@@ -350,7 +367,7 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_replicated_kernel(Layou
             const int32_t d = tid * per + i;
             if (d < K) {
                 s_off[d] = run;
-                run += s_hist[d] + s_hist[K + d];
+                run += kh[d] + kh[K + d];
             }
         }
     }
@@ -358,7 +375,7 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_replicated_kernel(Layou
     // row bases of each wave of this tile: region start + rows in earlier
     // tiles + rows of earlier waves of this tile
     for (int32_t d = tid; d < K; d += T_) {
-        int32_t run = s_off[d] + s_hist[d];
+        int32_t run = s_off[d] + kh[d];
 #pragma unroll
         for (int v_ = 0; v_ < kLayoutWaves; ++v_) {
             const int32_t c = s_wh[v_ * K + d];
@@ -371,37 +388,33 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_replicated_kernel(Layou
     tile_ranks<kLayoutWaves, LR, EORD>(p, ev, s_wh, q);
     store_positions<kLayoutWaves, LR, false>(a, tile, q, &bad_pos);
 
-    // rows with a key of rank d in a per-key array v (rank order: v[d])
-    const auto rank_sum = [&](const int32_t* v_, int32_t d) -> int32_t {
-        if (!EORD) return v_[d];
+    // rows to rank d before this tile (half 0) or in total (half 1)
+    const auto rank_rows = [&](int32_t d, bool total) -> int32_t {
+        if (!EORD) return s_rk[d] + (total ? s_rk[R + d] : 0);
         int32_t c = 0;
-        for (int32_t e = d * epr; e < (d + 1) * epr; ++e) c += v_[e];
+        for (int32_t e = d * epr; e < (d + 1) * epr; ++e) c += s_hist[e] + (total ? s_hist[E + e] : 0);
         return c;
     };
     const int64_t tok0 = tile * p.tile_tokens;
     if (tok0 % p.tps == 0)
-        for (int32_t d = tid; d < R; d += T_) a.send_offset[(tok0 / p.tps) * R + d] = rank_sum(s_hist, d);
+        for (int32_t d = tid; d < R; d += T_) a.send_offset[(tok0 / p.tps) * R + d] = rank_rows(d, false);
     if (a.chunk_offset != nullptr && tok0 % p.tpc == 0)
-        for (int32_t d = tid; d < R; d += T_) a.chunk_offset[(tok0 / p.tpc) * R + d] = rank_sum(s_hist, d);
-    for (int i = tid; i < n_e; i += T_) a.expert_count[e_lo + i] = s_eh[i];
+        for (int32_t d = tid; d < R; d += T_) a.chunk_offset[(tok0 / p.tpc) * R + d] = rank_rows(d, false);
+    {   // each workgroup writes a slice of the expert totals
+        const int32_t e_per = (E + (int32_t)gridDim.x - 1) / (int32_t)gridDim.x;
+        const int32_t e_lo = (int64_t)tile * e_per < E ? (int32_t)tile * e_per : E;
+        const int32_t e_hi = E - e_lo < e_per ? E : e_lo + e_per;
+        for (int32_t e = e_lo + tid; e < e_hi; e += T_) a.expert_count[e] = s_hist[e] + s_hist[E + e];
+    }
     if (tile == 0) {
         for (int32_t d = tid; d < R; d += T_) {
-            int32_t c = 0;
-            if (!EORD) {
-                c = s_hist[K + d];                         // tile 0: every row is "not before"
-            } else {
-                for (int32_t e = d * epr; e < (d + 1) * epr; ++e) c += s_hist[K + e];
-            }
-            a.rank_count[d] = c;
+            a.rank_count[d] = rank_rows(d, true);
             a.recv_offset[d] = s_off[EORD ? d * epr : d];
         }
         if (tid == 0) a.recv_offset[R] = (int32_t)p.rows;
-        if (EORD) {
-            for (int32_t e = tid; e < E; e += T_) {
-                a.expert_count[e] = s_hist[K + e];
-                if (a.expert_offset != nullptr) a.expert_offset[e] = s_off[e];
-            }
-            if (tid == 0 && a.expert_offset != nullptr) a.expert_offset[E] = (int32_t)p.rows;
+        if (EORD && a.expert_offset != nullptr) {
+            for (int32_t e = tid; e < E; e += T_) a.expert_offset[e] = s_off[e];
+            if (tid == 0) a.expert_offset[E] = (int32_t)p.rows;
         }
     }
     if (bad) raise_status(a.status, UBEP_ERR_BAD_EXPERT_ID);
