@@ -78,10 +78,14 @@ __global__ __launch_bounds__(kGemmThreads, 2) void expert_linear_kernel(ExpertAr
     constexpr int kBM = BM;
     constexpr int kLoadsX = loads_x<BM>();
     constexpr int JT = BM / 32;                          // 16-row MFMA tiles per wave (two waves share the rows)
-    __shared__ __attribute__((aligned(16))) uint16_t s_w[kBN * kLdsStride];
-    __shared__ __attribute__((aligned(16))) uint16_t s_x[BM * kLdsStride];
-    __shared__ int32_t s_wsum[kGemmThreads / 64];
-    __shared__ int32_t s_sel[2];
+    // two LDS stages of (weights, receive rows): step kt+1 is written while
+    // step kt is multiplied, one barrier per k step
+    extern __shared__ __attribute__((aligned(16))) uint16_t s_dyn[];
+    constexpr int kStage = (kBN + BM) * kLdsStride;
+    // the prologue's words live in stage 1, first written after the barrier
+    // that follows their last read (two workgroups then fit a CU's 160 KB)
+    int32_t* s_wsum = reinterpret_cast<int32_t*>(s_dyn + kStage);
+    int32_t* s_sel = s_wsum + kGemmThreads / 64;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int32_t m = (int32_t)blockIdx.y;
@@ -170,8 +174,9 @@ __global__ __launch_bounds__(kGemmThreads, 2) void expert_linear_kernel(ExpertAr
         for (int i = 0; i < kLoadsX; ++i)
             dx[i] = __builtin_amdgcn_raw_buffer_load_b128(rx, xoff[i], xso, 0);
     };
-    auto stage = [&](const u32x4 (&sw)[kLoadsW], const u32x4 (&sx)[kLoadsX]) {
-        __syncthreads();                                 // the last step's fragments are read
+    auto write_stage = [&](int b, const u32x4 (&sw)[kLoadsW], const u32x4 (&sx)[kLoadsX]) {
+        uint16_t* s_w = s_dyn + b * kStage;
+        uint16_t* s_x = s_w + kBN * kLdsStride;
 #pragma unroll
         for (int i = 0; i < kLoadsW; ++i) {
             const int q = tid + kGemmThreads * i;
@@ -182,7 +187,6 @@ __global__ __launch_bounds__(kGemmThreads, 2) void expert_linear_kernel(ExpertAr
             const int q = tid + kGemmThreads * i;
             *reinterpret_cast<u32x4*>(&s_x[lds_at(q / kVecPerRow, q % kVecPerRow)]) = sx[i];
         }
-        __syncthreads();
     };
     f32x4 acc[4][JT];
 #pragma unroll
@@ -192,7 +196,9 @@ __global__ __launch_bounds__(kGemmThreads, 2) void expert_linear_kernel(ExpertAr
 
     const int wn = (wave & 1) * 64, wm = (wave >> 1) * (BM / 2);
     const int fr = lane & 15, fk = (lane >> 4) * 8;      // fragment row and channel offset
-    auto multiply = [&]() {
+    auto multiply = [&](int b) {
+        const uint16_t* s_w = s_dyn + b * kStage;
+        const uint16_t* s_x = s_w + kBN * kLdsStride;
 #pragma unroll
         for (int ks = 0; ks < kBK; ks += 32) {
             bf16x8 fa[4], fb[JT];
@@ -210,16 +216,24 @@ __global__ __launch_bounds__(kGemmThreads, 2) void expert_linear_kernel(ExpertAr
         }
     };
     const int64_t nk = n_ksteps;
+    // stage 0 holds step kt when an even step starts, with steps kt+1 (pw1)
+    // and kt+2 (pw0) in flight; odd steps mirror it
     load_step(0, pw0, px0);
     if (nk > 1) load_step(1, pw1, px1);
+    write_stage(0, pw0, px0);
+    if (nk > 2) load_step(2, pw0, px0);
+    __syncthreads();
     for (int64_t kt = 0; kt < nk; kt += 2) {
-        stage(pw0, px0);
-        if (kt + 2 < nk) load_step(kt + 2, pw0, px0);
-        multiply();
+        multiply(0);
         if (kt + 1 >= nk) break;
-        stage(pw1, px1);
+        write_stage(1, pw1, px1);                        // stage 1's last reader passed the barrier
         if (kt + 3 < nk) load_step(kt + 3, pw1, px1);
-        multiply();
+        __syncthreads();
+        multiply(1);
+        if (kt + 2 >= nk) break;
+        write_stage(0, pw0, px0);
+        if (kt + 4 < nk) load_step(kt + 4, pw0, px0);
+        __syncthreads();
     }
 
     // ---- epilogue: lane holds channels n .. n+3 of row r for each (i, j)
@@ -261,6 +275,14 @@ hipError_t launch_expert_pack(int32_t E, int64_t N, int64_t H, const void* w, vo
                          static_cast<const u32x4*>(w), static_cast<u32x4*>(packed), N, H, total);
 }
 
+static size_t expert_lds_bytes(int bm) { return (size_t)2 * (kBN + bm) * kLdsStride * sizeof(uint16_t); }
+
+// The two-stage tiles take more than the default 64 KB of LDS per workgroup.
+static hipError_t set_expert_lds(void (*kernel)(ExpertArgs), size_t bytes) {
+    return hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+}
+
 hipError_t launch_expert_linear(int32_t E, int64_t H, int64_t N, int64_t n_rows,
                                 const int32_t* expert_offset, const void* x, const void* w, void* y,
                                 uint32_t* status, hipStream_t stream) {
@@ -281,9 +303,13 @@ hipError_t launch_expert_linear(int32_t E, int64_t H, int64_t N, int64_t n_rows,
     // they must.  The pending timing pair spans both launches.
     const LaunchEvents ev = take_launch_events();
     const dim3 block(kGemmThreads);
+    const size_t lds_short = expert_lds_bytes(kBShort), lds_tall = expert_lds_bytes(kBTall);
+    hipError_t e = set_expert_lds(expert_linear_kernel<kBShort>, lds_short);
+    if (e == hipSuccess) e = set_expert_lds(expert_linear_kernel<kBTall>, lds_tall);
+    if (e != hipSuccess) return e;
     a.rows_class = 1;                                 // at most one 128-row tile per expert
-    hipError_t e = launch_kernel_ev(expert_linear_kernel<kBShort>, dim3((unsigned)(N / kBN), (unsigned)E),
-                                    block, 0, stream, ev.start, nullptr, a);
+    e = launch_kernel_ev(expert_linear_kernel<kBShort>, dim3((unsigned)(N / kBN), (unsigned)E), block,
+                         lds_short, stream, ev.start, nullptr, a);
     if (e != hipSuccess) return e;
     // experts above 128 rows: at most n_rows / 129 of them, each with one partial tile
     const int64_t tall_e = n_rows / (kBShort + 1) < E ? n_rows / (kBShort + 1) : E;
@@ -291,7 +317,7 @@ hipError_t launch_expert_linear(int32_t E, int64_t H, int64_t N, int64_t n_rows,
     a.rows_class = 2;
     return launch_kernel_ev(expert_linear_kernel<kBTall>,
                             dim3((unsigned)(N / kBN), (unsigned)(tall_tiles > 0 ? tall_tiles : 1)),
-                            block, 0, stream, nullptr, ev.stop, a);
+                            block, lds_tall, stream, nullptr, ev.stop, a);
 }
 
 }  // namespace ubep
