@@ -13,13 +13,16 @@
 //
 // A dense contraction per expert, so it runs on the matrix cores:
 // v_mfma_f32_16x16x32_bf16 (gfx950) with fp32 accumulation.  A workgroup of
-// 4 waves computes a 128 (output channels) x 128 (rows) tile of one expert;
-// each wave a 64 x 64 quarter as 4 x 4 MFMA tiles.  The weight rows are the
-// MFMA's A operand and the receive rows its B operand, both read as 16-byte
-// runs of 8 channels, so each lane's 4 accumulator values are 4 consecutive
-// output channels of one row (one 8-byte store).  k steps of 64 channels are
-// staged through LDS (16-byte units swizzled per row pair), and the next two steps'
-// global loads are in flight while the current step's MFMAs run.
+// 8 waves computes a 256 (output channels) x BM (rows, 128 or 192) tile of
+// one expert; each wave a 64 x BM/2 part as 4 x BM/32 MFMA tiles.  The wide
+// output tile matters: every output tile re-reads the expert's receive rows
+// from L2, and at 128 channels that re-read traffic equalled the weight
+// stream itself.  The weight rows are the MFMA's A operand and the receive
+// rows its B operand, both read as 16-byte runs of 8 channels, so each lane's
+// 4 accumulator values are 4 consecutive output channels of one row (one
+// 8-byte store).  k steps of 64 channels are staged through two LDS stages
+// (16-byte units swizzled per row pair): step s+1 is written while step s is
+// multiplied, and the weight loads run two steps ahead.
 //
 // Tiles: blockIdx.x is the output-channel tile, blockIdx.y a row tile counted
 // over all experts in expert order (expert e owns ceil(count_e / 128) of
@@ -28,6 +31,8 @@
 // and this kernel.  Rows past the run's end are loaded as zeros and not
 // stored.  Consecutive workgroups share a row tile and walk the output
 // channels, so the tile's receive rows stay in L2 while the weights stream.
+#include <utility>
+
 #include "launch.h"
 #include "rows.h"
 
@@ -36,11 +41,14 @@ namespace ubep {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kGemmThreads = 256;
-constexpr int kBN = 128;                 // output channels per tile
+constexpr int kGemmThreads = 512;       // 8 waves: 4 along the output channels x 2 along the rows
+constexpr int kBN = 256;                 // output channels per tile
+constexpr int kPackN = 128;              // output channels per packed weight block
 constexpr int kBShort = 128;             // rows per tile of experts with at most this many rows
 constexpr int kBTall = 192;              // rows per tile of the others
 constexpr int kBK = 64;                  // channels per k step
+constexpr int kWDepth = 2;               // weight steps in flight (register sets)
+constexpr int kUnroll = kWDepth % 2 == 0 ? kWDepth : 2 * kWDepth;   // a multiple of 2 and kWDepth
 constexpr int kLdsStride = kBK;          // bf16 per LDS row: 128 bytes, 16-byte units swizzled
 static_assert(kBK == 64, "the LDS swizzle permutes the 8 units of a 64-channel row");
 
@@ -153,23 +161,39 @@ __global__ __launch_bounds__(kGemmThreads, 2) void expert_linear_kernel(ExpertAr
     // packed weights: the (expert, output tile) block holds the tile's k steps
     // back to back, each a row-major 128 x 64 bf16 block of 16 KB
     const int64_t n_ksteps = a.H / kBK;
-    const u32x4* wblk = a.w + ((int64_t)e * (a.N / kBN) + blockIdx.x) * n_ksteps * (kBN * kVecPerRow);
-    const __amdgpu_buffer_rsrc_t rw = row_rsrc(wblk, n_ksteps * kBN * kBK * 2);
+    // this tile's output channels are two packed blocks, adjacent in memory
+    // (one when N is an odd number of blocks and this is the last tile: the
+    // second half then loads zeros and stores nothing)
+    const int64_t nblk = a.N / kPackN, b0 = 2 * (int64_t)blockIdx.x;
+    const int64_t halves = nblk - b0 < 2 ? nblk - b0 : 2;
+    const int64_t blk_bytes = n_ksteps * kPackN * kBK * 2;
+    const u32x4* wblk = a.w + ((int64_t)e * nblk + b0) * n_ksteps * (kPackN * kVecPerRow);
+    const __amdgpu_buffer_rsrc_t rw = row_rsrc(wblk, halves * blk_bytes);
     const __amdgpu_buffer_rsrc_t rx = row_rsrc(a.x + r_lo * nvh, n_x * row_bytes);
-    // two k steps of global loads in flight: while step kt's fragments are
-    // multiplied, the loads of steps kt+1 and kt+2 are outstanding
-    u32x4 pw0[kLoadsW], px0[kLoadsX], pw1[kLoadsW], px1[kLoadsX];
+    // The weights come from HBM and get kWDepth register sets: the loads of
+    // step s+1+kWDepth are issued while step s is multiplied.  The receive
+    // rows are mostly L2 hits (every output tile of the expert reads them)
+    // and get one set, loaded a step ahead.
+    u32x4 pw[kWDepth][kLoadsW], px[kLoadsX];
     int32_t xoff[kLoadsX];
 #pragma unroll
     for (int i = 0; i < kLoadsX; ++i) {
         const int q = tid + kGemmThreads * i;            // kBM rows x kVecPerRow vectors
         xoff[i] = (q / kVecPerRow) * row_bytes + (q % kVecPerRow) * 16;
     }
-    auto load_step = [&](int64_t kt, u32x4 (&dw)[kLoadsW], u32x4 (&dx)[kLoadsX]) {
-        const int32_t wso = (int32_t)(kt * (kBN * kBK * 2)), xso = (int32_t)(kt * (kBK * 2));
+    constexpr int kVecPerBlock = kPackN * kVecPerRow;   // vectors of one block's k step
+    auto load_w = [&](int64_t kt, u32x4 (&dw)[kLoadsW]) {
+        const int32_t wso = (int32_t)(kt * (kPackN * kBK * 2));
 #pragma unroll
-        for (int i = 0; i < kLoadsW; ++i)   // weights: one contiguous 16 KB block per step
-            dw[i] = __builtin_amdgcn_raw_buffer_load_b128(rw, (tid + kGemmThreads * i) * 16, wso, 0);
+        for (int i = 0; i < kLoadsW; ++i) {  // a contiguous 16 KB run of each block per step
+            const int q = tid + kGemmThreads * i;
+            const int32_t half = q / kVecPerBlock;       // a constant per i
+            dw[i] = __builtin_amdgcn_raw_buffer_load_b128(
+                rw, (int32_t)(half * blk_bytes) + (q % kVecPerBlock) * 16, wso, 0);
+        }
+    };
+    auto load_x = [&](int64_t kt, u32x4 (&dx)[kLoadsX]) {
+        const int32_t xso = (int32_t)(kt * (kBK * 2));
 #pragma unroll
         for (int i = 0; i < kLoadsX; ++i)
             dx[i] = __builtin_amdgcn_raw_buffer_load_b128(rx, xoff[i], xso, 0);
@@ -194,7 +218,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void expert_linear_kernel(ExpertAr
 #pragma unroll
         for (int j = 0; j < JT; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-    const int wn = (wave & 1) * 64, wm = (wave >> 1) * (BM / 2);
+    const int wn = (wave & 3) * 64, wm = (wave >> 2) * (BM / 2);
     const int fr = lane & 15, fk = (lane >> 4) * 8;      // fragment row and channel offset
     auto multiply = [&](int b) {
         const uint16_t* s_w = s_dyn + b * kStage;
@@ -216,25 +240,32 @@ __global__ __launch_bounds__(kGemmThreads, 2) void expert_linear_kernel(ExpertAr
         }
     };
     const int64_t nk = n_ksteps;
-    // stage 0 holds step kt when an even step starts, with steps kt+1 (pw1)
-    // and kt+2 (pw0) in flight; odd steps mirror it
-    load_step(0, pw0, px0);
-    if (nk > 1) load_step(1, pw1, px1);
-    write_stage(0, pw0, px0);
-    if (nk > 2) load_step(2, pw0, px0);
+    // Step s multiplies LDS stage s % 2, writes step s+1 (weight set
+    // (s+1) % kWDepth, the receive-row set) into the other stage, whose last
+    // reader passed the previous barrier, and refills the two register sets
+    // it emptied.  Unrolled by kUnroll so that every set index is a constant.
+    auto step = [&](int64_t s_, auto jc) {
+        constexpr int J = decltype(jc)::value;
+        multiply(J % 2);
+        if (s_ + 1 < nk) {
+            write_stage((J + 1) % 2, pw[(J + 1) % kWDepth], px);
+            if (s_ + 2 < nk) load_x(s_ + 2, px);
+            if (s_ + 1 + kWDepth < nk) load_w(s_ + 1 + kWDepth, pw[(J + 1) % kWDepth]);
+        }
+        __syncthreads();
+    };
+    auto unrolled = [&]<int... J>(int64_t kt, std::integer_sequence<int, J...>) {
+        (void)((kt + J < nk && (step(kt + J, std::integral_constant<int, J>{}), true)) && ...);
+    };
+#pragma unroll
+    for (int d = 0; d < kWDepth; ++d)
+        if (d < nk) load_w(d, pw[d]);
+    load_x(0, px);
+    write_stage(0, pw[0], px);
+    if (kWDepth < nk) load_w(kWDepth, pw[0]);
+    if (1 < nk) load_x(1, px);
     __syncthreads();
-    for (int64_t kt = 0; kt < nk; kt += 2) {
-        multiply(0);
-        if (kt + 1 >= nk) break;
-        write_stage(1, pw1, px1);                        // stage 1's last reader passed the barrier
-        if (kt + 3 < nk) load_step(kt + 3, pw1, px1);
-        __syncthreads();
-        multiply(1);
-        if (kt + 2 >= nk) break;
-        write_stage(0, pw0, px0);
-        if (kt + 4 < nk) load_step(kt + 4, pw0, px0);
-        __syncthreads();
-    }
+    for (int64_t kt = 0; kt < nk; kt += kUnroll) unrolled(kt, std::make_integer_sequence<int, kUnroll>{});
 
     // ---- epilogue: lane holds channels n .. n+3 of row r for each (i, j)
     const int64_t nq = a.N / 4;
@@ -245,7 +276,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void expert_linear_kernel(ExpertAr
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int64_t n = n0 + wn + 16 * i + (lane >> 4) * 4;
-            a.y[r * nq + n / 4] = pack_bf16x4(acc[i][j]);
+            if (n < a.N) a.y[r * nq + n / 4] = pack_bf16x4(acc[i][j]);
         }
     }
 }
@@ -258,12 +289,12 @@ __global__ __launch_bounds__(256) void expert_pack_kernel(const u32x4* __restric
                                                           int64_t H, int64_t total) {
     const int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;   // packed vector index
     if (v >= total) return;
-    const int64_t vpb = kBN * kVecPerRow;                // vectors per 128 x 64 block
+    const int64_t vpb = kPackN * kVecPerRow;                // vectors per 128 x 64 block
     const int64_t blk = v / vpb, in = v % vpb;
     const int64_t r = in / kVecPerRow, cv = in % kVecPerRow;
-    const int64_t ksteps = H / kBK, ntiles = N / kBN;
+    const int64_t ksteps = H / kBK, ntiles = N / kPackN;
     const int64_t kt = blk % ksteps, nt = (blk / ksteps) % ntiles, e = blk / (ksteps * ntiles);
-    const int64_t n = nt * kBN + r;
+    const int64_t n = nt * kPackN + r;
     packed[v] = w[(e * N + n) * (H / 8) + kt * kVecPerRow + cv];
 }
 
@@ -308,7 +339,7 @@ hipError_t launch_expert_linear(int32_t E, int64_t H, int64_t N, int64_t n_rows,
     if (e == hipSuccess) e = set_expert_lds(expert_linear_kernel<kBTall>, lds_tall);
     if (e != hipSuccess) return e;
     a.rows_class = 1;                                 // at most one 128-row tile per expert
-    e = launch_kernel_ev(expert_linear_kernel<kBShort>, dim3((unsigned)(N / kBN), (unsigned)E), block,
+    e = launch_kernel_ev(expert_linear_kernel<kBShort>, dim3((unsigned)((N + kBN - 1) / kBN), (unsigned)E), block,
                          lds_short, stream, ev.start, nullptr, a);
     if (e != hipSuccess) return e;
     // experts above 128 rows: at most n_rows / 129 of them, each with one partial tile
@@ -316,7 +347,7 @@ hipError_t launch_expert_linear(int32_t E, int64_t H, int64_t N, int64_t n_rows,
     const int64_t tall_tiles = (n_rows + kBTall - 1) / kBTall + tall_e;
     a.rows_class = 2;
     return launch_kernel_ev(expert_linear_kernel<kBTall>,
-                            dim3((unsigned)(N / kBN), (unsigned)(tall_tiles > 0 ? tall_tiles : 1)),
+                            dim3((unsigned)((N + kBN - 1) / kBN), (unsigned)(tall_tiles > 0 ? tall_tiles : 1)),
                             block, lds_tall, stream, nullptr, ev.stop, a);
 }
 
