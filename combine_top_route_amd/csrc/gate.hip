@@ -211,53 +211,65 @@ __global__ __launch_bounds__(kGateThreads) void gate_kernel(GateArgs a) {
 // ---------------------------------------------------------------- row kernel
 // Four tokens per wave: token r of a wave owns DPP row r (16 lanes), lane l of
 // the row holds its VPL consecutive logits [l*VPL, (l+1)*VPL) (VPL/4 16-byte
-// loads; a wave reads 4 rows back to back).  A candidate is one 64-bit key:
-// the logit mapped to an order-preserving unsigned word in the high half and
-// the inverted expert id in the low half, so "larger logit first, equal
-// logits to the lower id" is one unsigned comparison and a removed candidate
-// is key 0 (below every finite logit's key).  Each of the k selection rounds
-// is a 4-step rotate-within-row reduction over the lanes' best remaining keys
-// (DPP row_ror 8, 4, 2, 1: after the four steps every lane of the row holds
-// the row's maximum), instead of a wave-wide shuffle butterfly per token; each
-// lane keeps its three best keys, so the lane that wins a round only pops
-// (it rescans its VPL keys below its last pick only after giving all three).
+// loads; a wave reads 4 rows back to back).  Each lane keeps its three best
+// (logit, id) pairs, found with exact fp32 comparisons in ascending id order,
+// so that a strict comparison keeps the lower id among equal logits.  Each of
+// the k selection rounds finds the row's best remaining pair with two 4-step
+// rotate-within-row reductions, each step one DPP max or min instruction: the
+// largest logit as an order-preserving integer (-0 and +0 map to one value,
+// as fp32 compares them), then the lowest id among the lanes holding it.  The
+// lane that wins a round pops its best; it rescans its VPL logits below its
+// last pick only after giving all three.
 // Groups: a group spans `span` aligned lanes (gsize = span * VPL); the lanes'
-// top two keys are merged across the span with xor shuffles, and each lane
+// two best logits are merged across the span with xor shuffles, and each lane
 // ranks its group's score against the row's G = 16 / span groups.
 constexpr int kRowLanes = 16;
-constexpr int kRowTokensPerWave = 64 / kRowLanes;
 constexpr int kGateRowTokens = kGateThreads / kRowLanes;   // tokens per workgroup
 
-__device__ __forceinline__ uint64_t gate_key(float v, int32_t e) {
-    uint32_t u = __float_as_uint(v);
-    if ((u << 1) == 0u) u = 0u;      // -0 compares equal to +0: one key for both
-    const uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-    return ((uint64_t)ord << 32) | (uint32_t)~(uint32_t)e;
+// Finite fp32 -> int32 of the same order, with -0 and +0 both 0 (sign and
+// magnitude to two's complement); value_of inverts it (0 -> +0).
+__device__ __forceinline__ int32_t ord_of(float v) {
+    const int32_t s = __float_as_int(v);
+    return s < 0 ? -(s & 0x7FFFFFFF) : s;
 }
-__device__ __forceinline__ float key_value(uint64_t k) {
-    const uint32_t ord = (uint32_t)(k >> 32);
-    return __uint_as_float((ord & 0x80000000u) ? (ord & 0x7FFFFFFFu) : ~ord);
+__device__ __forceinline__ float value_of(int32_t o) {
+    return o < 0 ? __int_as_float((-o) | (int32_t)0x80000000) : __int_as_float(o);
 }
-__device__ __forceinline__ int32_t key_id(uint64_t k) { return (int32_t)~(uint32_t)k; }
 
+// Every lane of a 16-lane row receives the row's maximum (minimum).  DPP
+// row_ror n (dpp_ctrl 0x120 + n) reads a lane of the same row for every n, so
+// no lane takes the bound_ctrl fill; the compiler folds each move into the
+// max (min) as one DPP instruction.
+constexpr int kDppRowRor = 0x120;       // row_ror:n = 0x120 + n
+constexpr int kDppRowBcast = 0x150;     // row_newbcast:n = 0x150 + n (every lane reads row lane n)
 template <int CTRL>
-__device__ __forceinline__ uint64_t dpp_u64(uint64_t k) {
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)k, CTRL, 0xF, 0xF, false);
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(k >> 32), CTRL, 0xF, 0xF, false);
-    return ((uint64_t)hi << 32) | lo;
+__device__ __forceinline__ int32_t dpp_i(int32_t x) { return __builtin_amdgcn_mov_dpp(x, CTRL, 0xF, 0xF, true); }
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) { return __int_as_float(dpp_i<CTRL>(__float_as_int(x))); }
+
+template <bool MAX>
+__device__ __forceinline__ int32_t row_reduce(int32_t x) {
+    int32_t o = dpp_i<kDppRowRor + 8>(x);
+    x = MAX ? max(x, o) : min(x, o);
+    o = dpp_i<kDppRowRor + 4>(x);
+    x = MAX ? max(x, o) : min(x, o);
+    o = dpp_i<kDppRowRor + 2>(x);
+    x = MAX ? max(x, o) : min(x, o);
+    o = dpp_i<kDppRowRor + 1>(x);
+    return MAX ? max(x, o) : min(x, o);
 }
 
-// Every lane of a 16-lane row receives the row's largest key.
-__device__ __forceinline__ uint64_t row_max(uint64_t k) {
-    constexpr int kRowRor = 0x120;   // DPP row_ror:n = 0x120 + n (rotate right within 16 lanes)
-    uint64_t o = dpp_u64<kRowRor + 8>(k);
-    k = o > k ? o : k;
-    o = dpp_u64<kRowRor + 4>(k);
-    k = o > k ? o : k;
-    o = dpp_u64<kRowRor + 2>(k);
-    k = o > k ? o : k;
-    o = dpp_u64<kRowRor + 1>(k);
-    return o > k ? o : k;
+// Insert (v, e) into a lane's sorted best three; (v, e) comes after every
+// pair already held that has an equal logit (ids ascend as the lane scans).
+__device__ __forceinline__ void insert3(float v, int32_t e, float& t1, int32_t& i1, float& t2,
+                                        int32_t& i2, float& t3, int32_t& i3) {
+    const bool g1 = v > t1, g2 = v > t2, g3 = v > t3;
+    t3 = g2 ? t2 : (g3 ? v : t3);
+    i3 = g2 ? i2 : (g3 ? e : i3);
+    t2 = g1 ? t1 : (g2 ? v : t2);
+    i2 = g1 ? i1 : (g2 ? e : i2);
+    t1 = g1 ? v : t1;
+    i1 = g1 ? e : i1;
 }
 
 // Per-tile counts the gate hands to the layout (ubep_gate_layout): rows per
@@ -279,45 +291,40 @@ __global__ __launch_bounds__(kGateThreads) void gate_rows_kernel(GateArgs a, int
         for (int i = threadIdx.x; i < gc.R; i += kGateThreads) s_rc[i] = 0;
         for (int i = threadIdx.x; i < a.E; i += kGateThreads) s_ec[i] = 0;
     }
+    constexpr float kNone = -__builtin_huge_valf();    // an empty slot: below every finite logit
+    constexpr int32_t kNoId = 0x7fffffff;
     const int lane = threadIdx.x & 63;
     const int rl = lane & (kRowLanes - 1);                  // lane within the token's row
     const int64_t t = (int64_t)blockIdx.x * kGateRowTokens + (threadIdx.x >> 4);
     const bool live = t < a.T;
     const float4* zr = reinterpret_cast<const float4*>(a.logits + (live ? t : 0) * a.E) + rl * (VPL / 4);
-    float4 z4[VPL / 4];
-#pragma unroll
-    for (int i = 0; i < VPL / 4; ++i) z4[i] = zr[i];
-    uint64_t key[VPL];
+    float z[VPL];
 #pragma unroll
     for (int i = 0; i < VPL / 4; ++i) {
-        const int32_t e0 = rl * VPL + 4 * i;
-        key[4 * i] = gate_key(z4[i].x, e0);
-        key[4 * i + 1] = gate_key(z4[i].y, e0 + 1);
-        key[4 * i + 2] = gate_key(z4[i].z, e0 + 2);
-        key[4 * i + 3] = gate_key(z4[i].w, e0 + 3);
+        const float4 q = zr[i];
+        z[4 * i] = q.x;
+        z[4 * i + 1] = q.y;
+        z[4 * i + 2] = q.z;
+        z[4 * i + 3] = q.w;
     }
+    const int32_t id0 = rl * VPL;
 
-    // the lane's best three keys (its two best also give the group score)
-    uint64_t t1 = 0, t2 = 0, t3 = 0;
+    // the lane's best three (its two best also give the group score)
+    float t1 = kNone, t2 = kNone, t3 = kNone;
+    int32_t i1 = kNoId, i2 = kNoId, i3 = kNoId;
 #pragma unroll
-    for (int i = 0; i < VPL; ++i) {
-        const uint64_t k_ = key[i];
-        const bool g1 = k_ > t1, g2 = k_ > t2, g3 = k_ > t3;
-        t3 = g2 ? t2 : (g3 ? k_ : t3);
-        t2 = g1 ? t1 : (g2 ? k_ : t2);
-        t1 = g1 ? k_ : t1;
-    }
+    for (int i = 0; i < VPL; ++i) insert3(z[i], id0 + i, t1, i1, t2, i2, t3, i3);
     if (a.groups > 1) {
-        // the group's best two across its span of lanes
-        uint64_t b1 = t1, b2 = t2;
+        // the group's two best logits across its span of lanes (values only:
+        // the score does not depend on which of equal logits is taken)
+        float b1 = t1, b2 = t2;
         for (int o = 1; o < span; o <<= 1) {
-            const uint64_t c1 = __shfl_xor(b1, o, 64), c2 = __shfl_xor(b2, o, 64);
-            const uint64_t hi1 = b1 > c1 ? b1 : c1, lo1 = b1 > c1 ? c1 : b1;
-            const uint64_t hi2 = b2 > c2 ? b2 : c2;
-            b1 = hi1;
+            const float c1 = __shfl_xor(b1, o, 64), c2 = __shfl_xor(b2, o, 64);
+            const float lo1 = b1 > c1 ? c1 : b1, hi2 = b2 > c2 ? b2 : c2;
+            b1 = b1 > c1 ? b1 : c1;
             b2 = lo1 > hi2 ? lo1 : hi2;
         }
-        const float score = key_value(b1) + key_value(b2);   // one fp32 addition
+        const float score = b1 + b2;                        // one fp32 addition
         const int32_t G = kRowLanes / span, g = rl / span;
         const int row0 = lane & ~(kRowLanes - 1);
         int32_t rank = 0;
@@ -325,51 +332,62 @@ __global__ __launch_bounds__(kGateThreads) void gate_rows_kernel(GateArgs a, int
             const float sh = __shfl(score, row0 + h * span, 64);
             rank += (sh > score || (sh == score && h < g)) ? 1 : 0;
         }
-        if (rank >= a.keep) t1 = t2 = t3 = 0;              // a dropped group offers nothing
+        if (rank >= a.keep) t1 = t2 = t3 = kNone;          // a dropped group offers nothing
     }
 
-    // k rounds: the row's best remaining key; its owner pops it.  A lane that
-    // has given its three may hold more (below its last pick): when any lane
+    // k rounds: the row's best remaining pair; its owner pops it.  A lane that
+    // has given its three may hold more (after its last pick): when any lane
     // of the wave is in that state, those lanes rescan for their next three.
-    bool more = t3 != 0;          // this lane may hold candidates past t3
-    uint64_t last = 0;            // this lane's last pick
-    uint64_t mine = 0, top = 0;
+    bool more = t3 != kNone;      // this lane may hold candidates past t3
+    float last_v = 0.0f;          // this lane's last pick
+    int32_t last_i = 0;
+    int32_t mine_o = 0, mine_i = 0, top_o = 0;
     for (int32_t j = 0; j < a.k; ++j) {
-        const uint64_t best = row_max(t1);
-        if (j == 0) top = best;
-        if (rl == j) mine = best;
-        if (t1 == best && best != 0) {
-            last = best;
-            t1 = t2;
-            t2 = t3;
-            t3 = 0;
+        const int32_t o = ord_of(t1);
+        const int32_t m = row_reduce<true>(o);
+        const int32_t mi = row_reduce<false>(o == m ? i1 : kNoId);
+        if (j == 0) top_o = m;
+        if (rl == j) {
+            mine_o = m;
+            mine_i = mi;
         }
-        const bool refill = more && t1 == 0;
+        if (o == m && i1 == mi) {
+            last_v = t1;
+            last_i = i1;
+            t1 = t2;
+            i1 = i2;
+            t2 = t3;
+            i2 = i3;
+            t3 = kNone;
+            i3 = kNoId;
+        }
+        const bool refill = more && t1 == kNone;
         if (__any(refill)) {
             if (refill) {
 #pragma unroll
                 for (int i = 0; i < VPL; ++i) {
-                    const uint64_t k_ = key[i] < last ? key[i] : 0ull;
-                    const bool g1 = k_ > t1, g2 = k_ > t2, g3 = k_ > t3;
-                    t3 = g2 ? t2 : (g3 ? k_ : t3);
-                    t2 = g1 ? t1 : (g2 ? k_ : t2);
-                    t1 = g1 ? k_ : t1;
+                    const int32_t e = id0 + i;
+                    const bool after = z[i] < last_v || (z[i] == last_v && e > last_i);
+                    insert3(after ? z[i] : kNone, e, t1, i1, t2, i2, t3, i3);
                 }
-                more = t3 != 0;
+                more = t3 != kNone;
             }
         }
     }
 
     // weights over the selected experts, in fp32; the row's sum from its lane 0
     const bool sel = rl < a.k;
-    const float mv = key_value(mine), tv = key_value(top);
+    const float mv = value_of(mine_o), tv = value_of(top_o);
     float u = 0.0f;
     if (sel) u = a.norm == UBEP_GATE_SOFTMAX ? expf(mv - tv) : 1.0f / (1.0f + expf(-mv));
-    float sum = u;
-    for (int o = 1; o < kRowLanes; o <<= 1) sum += __shfl_xor(sum, o, 64);
-    sum = __shfl(sum, lane & ~(kRowLanes - 1), 64);
+    float sum = u;                                      // rotate-and-add within the row,
+    sum += dpp_f<kDppRowRor + 8>(sum);                  // then row lane 0's total for all
+    sum += dpp_f<kDppRowRor + 4>(sum);
+    sum += dpp_f<kDppRowRor + 2>(sum);
+    sum += dpp_f<kDppRowRor + 1>(sum);
+    sum = dpp_f<kDppRowBcast + 0>(sum);
     if (live && sel) {
-        a.idx[t * a.k + rl] = key_id(mine);
+        a.idx[t * a.k + rl] = mine_i;
         a.w[t * a.k + rl] = u / sum;
     }
     if constexpr (COUNT) {
@@ -378,7 +396,7 @@ __global__ __launch_bounds__(kGateThreads) void gate_rows_kernel(GateArgs a, int
         // tile's rows of the workspace arrays
         __syncthreads();
         if (live && sel) {
-            const uint32_t e = (uint32_t)key_id(mine);
+            const uint32_t e = (uint32_t)mine_i;
             atomicAdd(&s_rc[rank_of(e, gc.epr_magic)], 1);
             atomicAdd(&s_ec[e], 1);
         }
