@@ -244,26 +244,36 @@ __global__ __launch_bounds__(kGemmThreads, 2) void expert_linear_kernel(ExpertAr
     // (s+1) % kWDepth, the receive-row set) into the other stage, whose last
     // reader passed the previous barrier, and refills the two register sets
     // it emptied.  Unrolled by kUnroll so that every set index is a constant.
+    // Every load is unconditional, its step clamped to the last one (a repeat
+    // of the last step is an L2 hit): with no branch around a load, the
+    // compiler's wait counts stay exact, so a step waits only for the loads
+    // it consumes and not for the ones just issued for later steps.  The
+    // prologue issues in the steady state's order: W(s+1), X(s+1), W(s+2).
+    const int64_t last = nk - 1;
+    auto clamp = [&](int64_t s_) { return s_ < last ? s_ : last; };
     auto step = [&](int64_t s_, auto jc) {
         constexpr int J = decltype(jc)::value;
         multiply(J % 2);
-        if (s_ + 1 < nk) {
-            write_stage((J + 1) % 2, pw[(J + 1) % kWDepth], px);
-            if (s_ + 2 < nk) load_x(s_ + 2, px);
-            if (s_ + 1 + kWDepth < nk) load_w(s_ + 1 + kWDepth, pw[(J + 1) % kWDepth]);
-        }
+        write_stage((J + 1) % 2, pw[(J + 1) % kWDepth], px);   // step s+1 (unused after the last)
+        load_x(clamp(s_ + 2), px);
+        load_w(clamp(s_ + 1 + kWDepth), pw[(J + 1) % kWDepth]);
         __syncthreads();
     };
     auto unrolled = [&]<int... J>(int64_t kt, std::integer_sequence<int, J...>) {
         (void)((kt + J < nk && (step(kt + J, std::integral_constant<int, J>{}), true)) && ...);
     };
-#pragma unroll
-    for (int d = 0; d < kWDepth; ++d)
-        if (d < nk) load_w(d, pw[d]);
+    // (scheduling barriers keep that order: the compiler may not merge the
+    // groups and move a load the loop waits for behind one it does not)
+    load_w(0, pw[0]);
     load_x(0, px);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int d = 1; d < kWDepth; ++d) load_w(clamp(d), pw[d]);
+    __builtin_amdgcn_sched_barrier(0);
     write_stage(0, pw[0], px);
-    if (kWDepth < nk) load_w(kWDepth, pw[0]);
-    if (1 < nk) load_x(1, px);
+    load_x(clamp(1), px);
+    __builtin_amdgcn_sched_barrier(0);
+    load_w(clamp(kWDepth), pw[0]);
     __syncthreads();
     for (int64_t kt = 0; kt < nk; kt += kUnroll) unrolled(kt, std::make_integer_sequence<int, kUnroll>{});
 
