@@ -259,7 +259,10 @@ __global__ __launch_bounds__(kGemmThreads, 2) void expert_linear_kernel(ExpertAr
         load_w(clamp(s_ + 1 + kWDepth), pw[(J + 1) % kWDepth]);
         __syncthreads();
     };
-    auto unrolled = [&]<int... J>(int64_t kt, std::integer_sequence<int, J...>) {
+    auto steps = [&]<int... J>(int64_t kt, std::integer_sequence<int, J...>) {
+        (step(kt + J, std::integral_constant<int, J>{}), ...);
+    };
+    auto first_steps = [&]<int... J>(int64_t kt, std::integer_sequence<int, J...>) {
         (void)((kt + J < nk && (step(kt + J, std::integral_constant<int, J>{}), true)) && ...);
     };
     // (scheduling barriers keep that order: the compiler may not merge the
@@ -275,7 +278,11 @@ __global__ __launch_bounds__(kGemmThreads, 2) void expert_linear_kernel(ExpertAr
     __builtin_amdgcn_sched_barrier(0);
     load_w(clamp(kWDepth), pw[0]);
     __syncthreads();
-    for (int64_t kt = 0; kt < nk; kt += kUnroll) unrolled(kt, std::make_integer_sequence<int, kUnroll>{});
+    // whole groups of kUnroll steps in the loop (no exit between its steps,
+    // so the loop head sees one pattern of pending loads), the rest after it
+    int64_t kt = 0;
+    for (; kt + kUnroll <= nk; kt += kUnroll) steps(kt, std::make_integer_sequence<int, kUnroll>{});
+    first_steps(kt, std::make_integer_sequence<int, kUnroll>{});
 
     // ---- epilogue: lane holds channels n .. n+3 of row r for each (i, j)
     const int64_t nq = a.N / 4;
