@@ -24,13 +24,9 @@
 // (16-byte units swizzled per row pair): step s+1 is written while step s is
 // multiplied, and the weight loads run two steps ahead.
 //
-// Tiles: blockIdx.x is the output-channel tile, blockIdx.y a row tile counted
-// over all experts in expert order (expert e owns ceil(count_e / 128) of
-// them); each workgroup finds its expert from expert_offset with one
-// workgroup-wide scan, so no host round trip is needed between the layout
-// and this kernel.  Rows past the run's end are loaded as zeros and not
-// stored.  Consecutive workgroups share a row tile and walk the output
-// channels, so the tile's receive rows stay in L2 while the weights stream.
+// Rows past a run's end are loaded as zeros and not stored.  Consecutive
+// workgroups share a row tile and walk the output channels, so the tile's
+// receive rows stay in L2 while the weights stream.
 #include <utility>
 
 #include "launch.h"
@@ -71,7 +67,6 @@ struct ExpertArgs {
     uint32_t* status;
     int64_t H, N, n_rows;
     int32_t E;
-    int32_t rows_class;      // 0: every expert; 1: experts of at most kBShort rows; 2: the others
 };
 
 __device__ __forceinline__ uint2 pack_bf16x4(f32x4 v) {
@@ -81,75 +76,19 @@ __device__ __forceinline__ uint2 pack_bf16x4(f32x4 v) {
     return o;
 }
 
+// One tile: rows [r_lo, min(r_lo + BM, r_end)) of expert e (a run ending at
+// r_end), output channels [256 nt, 256 nt + 256).  Run by the whole workgroup.
 template <int BM>
-__global__ __launch_bounds__(kGemmThreads, 2) void expert_linear_kernel(ExpertArgs a) {
+__device__ __forceinline__ void expert_tile(const ExpertArgs& a, int32_t e, int64_t r_lo, int64_t r_end,
+                                            int64_t nt, uint16_t* s_dyn) {
     constexpr int kBM = BM;
     constexpr int kLoadsX = loads_x<BM>();
     constexpr int JT = BM / 32;                          // 16-row MFMA tiles per wave (two waves share the rows)
     // two LDS stages of (weights, receive rows): step kt+1 is written while
     // step kt is multiplied, one barrier per k step
-    extern __shared__ __attribute__((aligned(16))) uint16_t s_dyn[];
     constexpr int kStage = (kBN + BM) * kLdsStride;
-    // the prologue's words live in stage 1, first written after the barrier
-    // that follows their last read (two workgroups then fit a CU's 160 KB)
-    int32_t* s_wsum = reinterpret_cast<int32_t*>(s_dyn + kStage);
-    int32_t* s_sel = s_wsum + kGemmThreads / 64;
-
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int32_t m = (int32_t)blockIdx.y;
-    const int64_t n0 = (int64_t)blockIdx.x * kBN;
-
-    // ---- which expert and which of its row tiles this workgroup takes
-    // offsets must run non-decreasing from 0 within [0, n_rows]; an expert
-    // whose run is reversed gets no tiles, and workgroup (0, 0) reports any
-    // violation (the tiles are then no longer sure to cover every run)
-    int32_t cnt[kPerThreadE];
-    int32_t mine = 0;
-    bool bad_off = false;
-#pragma unroll
-    for (int i = 0; i < kPerThreadE; ++i) {
-        const int32_t e = tid * kPerThreadE + i;
-        int32_t c = 0;
-        if (e < a.E) {
-            const int32_t lo = a.eoff[e], hi = a.eoff[e + 1];
-            const int32_t rows = hi - lo;
-            if (rows < 0 || lo < 0 || (int64_t)hi > a.n_rows || (e == 0 && lo != 0)) bad_off = true;
-            const bool in_class = a.rows_class == 0 || (a.rows_class == 1) == (rows <= kBShort);
-            c = rows > 0 && in_class ? (rows + kBM - 1) / kBM : 0;
-        }
-        cnt[i] = c;
-        mine += c;
-    }
-    if (bad_off && blockIdx.x == 0 && blockIdx.y == 0 && a.rows_class <= 1)
-        raise_status(a.status, UBEP_ERR_BAD_POSITION);
-    int32_t inc = mine;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const int32_t u = __shfl_up(inc, o, 64);
-        if (lane >= o) inc += u;
-    }
-    if (lane == 63) s_wsum[wave] = inc;
-    if (tid == 0) s_sel[0] = -1;
-    __syncthreads();
-    int32_t run = inc - mine;
-    for (int i = 0; i < wave; ++i) run += s_wsum[i];
-#pragma unroll
-    for (int i = 0; i < kPerThreadE; ++i) {
-        if (cnt[i] > 0 && m >= run && m < run + cnt[i]) {
-            s_sel[0] = tid * kPerThreadE + i;
-            s_sel[1] = m - run;
-        }
-        run += cnt[i];
-    }
-    __syncthreads();
-    const int32_t e = s_sel[0];
-    if (e < 0) return;                                   // past the last tile (uniform)
-    const int64_t run_lo = a.eoff[e], r_end = a.eoff[e + 1];
-    if (run_lo < 0 || r_end > a.n_rows) {                // inconsistent offsets
-        if (tid == 0) raise_status(a.status, UBEP_ERR_BAD_POSITION);
-        return;
-    }
-    const int64_t r_lo = run_lo + (int64_t)s_sel[1] * kBM;
+    const int64_t n0 = nt * kBN;
 
     // ---- k loop
     // Buffer resources over the tile's 128 weight rows and its receive rows
@@ -164,7 +103,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void expert_linear_kernel(ExpertAr
     // this tile's output channels are two packed blocks, adjacent in memory
     // (one when N is an odd number of blocks and this is the last tile: the
     // second half then loads zeros and stores nothing)
-    const int64_t nblk = a.N / kPackN, b0 = 2 * (int64_t)blockIdx.x;
+    const int64_t nblk = a.N / kPackN, b0 = 2 * nt;
     const int64_t halves = nblk - b0 < 2 ? nblk - b0 : 2;
     const int64_t blk_bytes = n_ksteps * kPackN * kBK * 2;
     const u32x4* wblk = a.w + ((int64_t)e * nblk + b0) * n_ksteps * (kPackN * kVecPerRow);
@@ -298,6 +237,101 @@ __global__ __launch_bounds__(kGemmThreads, 2) void expert_linear_kernel(ExpertAr
     }
 }
 
+// The tile-selection words of the prologue sit in LDS stage 1 of both tile
+// heights, which a tile first writes after the barrier that ends its own
+// prologue (so every read of them has happened).
+constexpr int kSelAt = (kBN + kBTall) * kLdsStride;
+static_assert(kSelAt >= (kBN + kBShort) * kLdsStride && kSelAt + 64 <= 2 * (kBN + kBShort) * kLdsStride,
+              "the selection words lie in stage 1 of both tile heights");
+
+// Tiles: blockIdx.x is the output-channel tile, blockIdx.y a row tile: first
+// the 192-row tiles of the experts above 128 rows (the longer tiles start
+// first), then one 128-row tile per expert of 1 to 128 rows.  An expert whose
+// rows need two tiles streams its weights twice, so experts above 128 rows
+// (about half of them in a decode step of 128 rows per expert) take 192-row
+// tiles, while the others multiply no more zero rows than they must.  Each
+// workgroup finds its expert and tile from expert_offset with one
+// workgroup-wide scan, so no host round trip is needed between the layout
+// and this kernel.
+__global__ __launch_bounds__(kGemmThreads, 2) void expert_linear_kernel(ExpertArgs a) {
+    extern __shared__ __attribute__((aligned(16))) uint16_t s_dyn[];
+    constexpr int W = kGemmThreads / 64;
+    int32_t* s_wsum = reinterpret_cast<int32_t*>(s_dyn + kSelAt);   // [2][W]: tall, short
+    int32_t* s_sel = s_wsum + 2 * W;                                   // expert, tile within it
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int32_t m = (int32_t)blockIdx.y;
+
+    // offsets must run non-decreasing from 0 within [0, n_rows]; an expert
+    // whose run is reversed gets no tiles, and workgroup (0, 0) reports any
+    // violation (the tiles are then no longer sure to cover every run)
+    int32_t ct[kPerThreadE], cs[kPerThreadE];
+    int32_t mt = 0, ms = 0;
+    bool bad_off = false;
+#pragma unroll
+    for (int i = 0; i < kPerThreadE; ++i) {
+        const int32_t e = tid * kPerThreadE + i;
+        ct[i] = cs[i] = 0;
+        if (e < a.E) {
+            const int32_t lo = a.eoff[e], hi = a.eoff[e + 1];
+            const int32_t rows = hi - lo;
+            if (rows < 0 || lo < 0 || (int64_t)hi > a.n_rows || (e == 0 && lo != 0)) bad_off = true;
+            if (rows > kBShort) ct[i] = (rows + kBTall - 1) / kBTall;
+            else if (rows > 0) cs[i] = 1;
+        }
+        mt += ct[i];
+        ms += cs[i];
+    }
+    if (bad_off && blockIdx.x == 0 && blockIdx.y == 0) raise_status(a.status, UBEP_ERR_BAD_POSITION);
+    int32_t it = mt, is = ms;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int32_t ut = __shfl_up(it, o, 64), us = __shfl_up(is, o, 64);
+        if (lane >= o) {
+            it += ut;
+            is += us;
+        }
+    }
+    if (lane == 63) {
+        s_wsum[wave] = it;
+        s_wsum[W + wave] = is;
+    }
+    if (tid == 0) s_sel[0] = -1;
+    __syncthreads();
+    int32_t tall_total = 0, run_t = it - mt, run_s = is - ms;
+    for (int i = 0; i < W; ++i) {
+        tall_total += s_wsum[i];
+        if (i < wave) {
+            run_t += s_wsum[i];
+            run_s += s_wsum[W + i];
+        }
+    }
+    const bool tall = m < tall_total;                    // uniform
+    const int32_t mm = tall ? m : m - tall_total;
+#pragma unroll
+    for (int i = 0; i < kPerThreadE; ++i) {
+        const int32_t c = tall ? ct[i] : cs[i], r = tall ? run_t : run_s;
+        if (c > 0 && mm >= r && mm < r + c) {
+            s_sel[0] = tid * kPerThreadE + i;
+            s_sel[1] = mm - r;
+        }
+        run_t += ct[i];
+        run_s += cs[i];
+    }
+    __syncthreads();
+    const int32_t e = s_sel[0];
+    if (e < 0) return;                                   // past the last tile (uniform)
+    const int64_t run_lo = a.eoff[e], r_end = a.eoff[e + 1];
+    if (run_lo < 0 || r_end > a.n_rows) {                // inconsistent offsets
+        if (tid == 0) raise_status(a.status, UBEP_ERR_BAD_POSITION);
+        return;
+    }
+    const int64_t tile = s_sel[1];
+    if (tall)
+        expert_tile<kBTall>(a, e, run_lo + tile * kBTall, r_end, blockIdx.x, s_dyn);
+    else
+        expert_tile<kBShort>(a, e, run_lo + tile * kBShort, r_end, blockIdx.x, s_dyn);
+}
+
 // packed[e][nt][kt][r][c] = w[e][nt*128 + r][kt*64 + c]: every 128 x 64 block
 // that one k step of one output tile reads becomes 16 contiguous KB.  One
 // thread moves one 16-byte vector (8 channels).
@@ -323,13 +357,9 @@ hipError_t launch_expert_pack(int32_t E, int64_t N, int64_t H, const void* w, vo
                          static_cast<const u32x4*>(w), static_cast<u32x4*>(packed), N, H, total);
 }
 
+// two stages of the taller tile: more than the default 64 KB of LDS per workgroup
 static size_t expert_lds_bytes(int bm) { return (size_t)2 * (kBN + bm) * kLdsStride * sizeof(uint16_t); }
 
-// The two-stage tiles take more than the default 64 KB of LDS per workgroup.
-static hipError_t set_expert_lds(void (*kernel)(ExpertArgs), size_t bytes) {
-    return hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
-                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
-}
 
 hipError_t launch_expert_linear(int32_t E, int64_t H, int64_t N, int64_t n_rows,
                                 const int32_t* expert_offset, const void* x, const void* w, void* y,
@@ -344,28 +374,16 @@ hipError_t launch_expert_linear(int32_t E, int64_t H, int64_t N, int64_t n_rows,
     a.N = N;
     a.n_rows = n_rows;
     a.E = E;
-    // Two launches by expert size: an expert whose rows need two tiles
-    // streams its weights twice, so experts of more than 128 rows (about half
-    // of them in a decode step of 128 rows per expert) take 192-row tiles,
-    // while the others keep 128-row tiles and multiply no more zero rows than
-    // they must.  The pending timing pair spans both launches.
-    const LaunchEvents ev = take_launch_events();
-    const dim3 block(kGemmThreads);
-    const size_t lds_short = expert_lds_bytes(kBShort), lds_tall = expert_lds_bytes(kBTall);
-    hipError_t e = set_expert_lds(expert_linear_kernel<kBShort>, lds_short);
-    if (e == hipSuccess) e = set_expert_lds(expert_linear_kernel<kBTall>, lds_tall);
-    if (e != hipSuccess) return e;
-    a.rows_class = 1;                                 // at most one 128-row tile per expert
-    e = launch_kernel_ev(expert_linear_kernel<kBShort>, dim3((unsigned)((N + kBN - 1) / kBN), (unsigned)E), block,
-                         lds_short, stream, ev.start, nullptr, a);
-    if (e != hipSuccess) return e;
-    // experts above 128 rows: at most n_rows / 129 of them, each with one partial tile
+    // tall tiles: experts above 128 rows, at most n_rows / 129 of them, each
+    // with one partial tile; short tiles: at most one per expert
     const int64_t tall_e = n_rows / (kBShort + 1) < E ? n_rows / (kBShort + 1) : E;
-    const int64_t tall_tiles = (n_rows + kBTall - 1) / kBTall + tall_e;
-    a.rows_class = 2;
-    return launch_kernel_ev(expert_linear_kernel<kBTall>,
-                            dim3((unsigned)((N + kBN - 1) / kBN), (unsigned)(tall_tiles > 0 ? tall_tiles : 1)),
-                            block, lds_tall, stream, nullptr, ev.stop, a);
+    const int64_t tiles = (n_rows + kBTall - 1) / kBTall + tall_e + E;
+    const size_t lds = expert_lds_bytes(kBTall);
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(expert_linear_kernel),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    return launch_kernel(expert_linear_kernel, dim3((unsigned)((N + kBN - 1) / kBN), (unsigned)tiles),
+                         dim3(kGemmThreads), lds, stream, a);
 }
 
 }  // namespace ubep
