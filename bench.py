@@ -285,52 +285,53 @@ def measure(name: str, args, hev) -> dict:
                          norm=ubep.GATE_SIGMOID if w.recipe.weights == "sigmoid" else ubep.GATE_SOFTMAX)
     lpt = args.chunk_order == "lpt"
 
-    def call(cname):
-        st = torch.cuda.current_stream()    # the capture stream while a graph records
+    sdc = ubep._abi._shape(sd)               # the C struct, built once (host time per call)
+
+    def call(cname, st):
         if cname == "gate":
             ubep.ubep_gate(s.T, s.E, s.k, logits, b.topk_idx, b.topk_w, stream=st, **gate_args)
         elif cname == "gate_layout":
-            ubep.ubep_gate_layout(sd, logits, b.topk_idx, b.topk_w, b.pos, b.expert_count,
+            ubep.ubep_gate_layout(sdc, logits, b.topk_idx, b.topk_w, b.pos, b.expert_count,
                                   b.rank_count, b.recv_offset, b.send_offset, chunk_off, None, b.ws,
                                   stream=st, **gate_args)
         elif cname == "layout" and order == "expert":
-            ubep.ubep_layout_grouped(sd, b.topk_idx, b.pos, b.expert_count, expert_off, b.rank_count,
+            ubep.ubep_layout_grouped(sdc, b.topk_idx, b.pos, b.expert_count, expert_off, b.rank_count,
                                      b.recv_offset, b.send_offset, chunk_off, None, b.ws, st)
         elif cname == "layout":
-            ubep.ubep_layout(sd, b.topk_idx, b.pos, b.expert_count, b.rank_count, b.recv_offset,
+            ubep.ubep_layout(sdc, b.topk_idx, b.pos, b.expert_count, b.rank_count, b.recv_offset,
                              b.send_offset, chunk_off, None, b.ws, st)
         elif cname == "layout_dispatch":
-            ubep.ubep_layout_dispatch(sd, b.topk_idx, b.x, b.pos, b.expert_count, b.rank_count,
+            ubep.ubep_layout_dispatch(sdc, b.topk_idx, b.x, b.pos, b.expert_count, b.rank_count,
                                       b.recv_offset, b.send_offset, chunk_off, None, b.recv, b.ws,
                                       st)
         elif cname == "expert":
-            ubep.ubep_expert_linear(sd, s.H, expert_off, b.recv, wpacked, yexp, b.ws, st)
+            ubep.ubep_expert_linear(sdc, s.H, expert_off, b.recv, wpacked, yexp, b.ws, st)
         elif cname == "sentinel":
-            ubep.ubep_dispatch_combine_sentinel(sd, b.x, b.pos, b.topk_w, b.recv, b.out, b.ws,
+            ubep.ubep_dispatch_combine_sentinel(sdc, b.x, b.pos, b.topk_w, b.recv, b.out, b.ws,
                                                 stream=st)
         elif cname == "chunked":
-            ubep.ubep_dispatch_combine_chunked(sd, b.x, b.pos, b.topk_w, b.recv, b.out, None, b.ws,
+            ubep.ubep_dispatch_combine_chunked(sdc, b.x, b.pos, b.topk_w, b.recv, b.out, None, b.ws,
                                                stream=st, **(dict(chunk_offset=chunk_off,
                                                                   rank_count=b.rank_count)
                                                              if lpt else {}))
         elif cname == "dispatch":
-            ubep.ubep_dispatch(sd, dtype, b.x, b.pos, b.recv, b.recv_scale, b.ws, st)
+            ubep.ubep_dispatch(sdc, dtype, b.x, b.pos, b.recv, b.recv_scale, b.ws, st)
         else:
-            ubep.ubep_combine(sd, yexp if moe else b.y, b.pos, b.topk_w, b.out, b.ws, st)
+            ubep.ubep_combine(sdc, yexp if moe else b.y, b.pos, b.topk_w, b.out, b.ws, st)
 
     def step(timed=None):
         """One step.  `timed` maps a call name (or 'identity', the fp8 identity
         expert between dispatch and combine) to a (start, stop) event pair that
         the call's kernel launch records at its own start and end."""
+        st = torch.cuda.current_stream().cuda_stream   # the capture stream while a graph records
         for cname in calls:
             if timed and cname in timed:
                 ubep.ubep_time_next_launch(*timed[cname])
-            call(cname)
+            call(cname, st)
             if cname == "dispatch" and fp8:
                 if timed and "identity" in timed:
                     ubep.ubep_time_next_launch(*timed["identity"])
-                ubep.ubep_identity_expert_fp8(s.T * s.k, s.H, b.recv, b.recv_scale, b.y,
-                                              torch.cuda.current_stream())
+                ubep.ubep_identity_expert_fp8(s.T * s.k, s.H, b.recv, b.recv_scale, b.y, st)
 
     def pairs(n):
         return [hev.pair() for _ in range(n)]
