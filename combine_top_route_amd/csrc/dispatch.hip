@@ -11,18 +11,28 @@ namespace ubep {
 
 constexpr int kRowBlock = 256;
 
-template <int G, int VPT, bool NT>
+// Blocks from nt_from on (the last ones to start) write their rows with
+// non-temporal stores: the rows written last would otherwise still sit dirty
+// in the L2s when the kernel ends, and the next kernel's loads would pay for
+// writing them back.  The tail is about twice the L2s' 32 MB, written while
+// the grid drains and HBM has room.
+constexpr int64_t kNtTailBytes = 64ll << 20;
+
+template <int G, int VPT>
 __global__ __launch_bounds__(kRowBlock) void dispatch_bf16_kernel(const u32x4* __restrict__ x,
                                                                   const int32_t* __restrict__ pos,
                                                                   u32x4* __restrict__ recv,
                                                                   int64_t T, int32_t k, int64_t nvec,
                                                                   int64_t n_rows, uint32_t* status,
-                                                                  uint32_t n_static) {
+                                                                  uint32_t n_static, uint32_t nt_from) {
     constexpr int TPB = kRowBlock / G;
     const uint32_t blk = claim_block(status + kHdrDispatchTicket, n_static, status);
     const int64_t t = (int64_t)blk * TPB + threadIdx.x / G;
     if (t >= T) return;
-    dispatch_row_bf16<G, VPT, NT>(x, pos, recv, t, k, nvec, n_rows, threadIdx.x % G, status);
+    if (blk >= nt_from)
+        dispatch_row_bf16<G, VPT, true>(x, pos, recv, t, k, nvec, n_rows, threadIdx.x % G, status);
+    else
+        dispatch_row_bf16<G, VPT, false>(x, pos, recv, t, k, nvec, n_rows, threadIdx.x % G, status);
 }
 
 template <int G>
@@ -49,16 +59,19 @@ hipError_t launch_dispatch_bf16(const Plan& p, const void* x, const int32_t* pos
         const int64_t blocks = (p.T + TPB - 1) / TPB;
         int64_t n_static = 0;
         const hipError_t e = resident_blocks(
-            reinterpret_cast<const void*>(dispatch_bf16_kernel<GG, VV, false>), kRowBlock, 0, &n_static);
+            reinterpret_cast<const void*>(dispatch_bf16_kernel<GG, VV>), kRowBlock, 0, &n_static);
         if (e != hipSuccess) return e;
         // start-order tickets only when later workgroups are many more than
         // the first resident wave (long grids drift apart across XCDs); with
         // a grid of a few waves they cost more than they save
         if (blocks < kTicketMinWaves * n_static) n_static = blocks;
-        return launch_kernel(dispatch_bf16_kernel<GG, VV, false>, dim3((unsigned)blocks),
+        const int64_t block_bytes = (int64_t)TPB * p.k * p.H * 2;   // receive rows a block writes
+        const int64_t nt_blocks = (kNtTailBytes + block_bytes - 1) / block_bytes;
+        const int64_t nt_from = blocks > nt_blocks ? blocks - nt_blocks : 0;
+        return launch_kernel(dispatch_bf16_kernel<GG, VV>, dim3((unsigned)blocks),
                              dim3(kRowBlock), 0, stream, static_cast<const u32x4*>(x), pos,
                              static_cast<u32x4*>(recv), p.T, p.k, p.H / 8, p.rows, status,
-                             (uint32_t)n_static);
+                             (uint32_t)n_static, (uint32_t)nt_from);
     };
     return with_group(G, VPT, go);
 }
