@@ -78,7 +78,11 @@ __device__ __forceinline__ uint2 pack_bf16x4(f32x4 v) {
 
 // One tile: rows [r_lo, min(r_lo + BM, r_end)) of expert e (a run ending at
 // r_end), output channels [256 nt, 256 nt + 256).  Run by the whole workgroup.
-template <int BM>
+// NTW: the expert has this one row tile, so its weights are read once and
+// are loaded non-temporally (they then do not push out the receive rows,
+// which every output tile of the expert reads again); an expert with several
+// row tiles keeps its weights cacheable for the others.
+template <int BM, bool NTW>
 __device__ __forceinline__ void expert_tile(const ExpertArgs& a, int32_t e, int64_t r_lo, int64_t r_end,
                                             int64_t nt, uint16_t* s_dyn) {
     constexpr int kBM = BM;
@@ -128,7 +132,7 @@ __device__ __forceinline__ void expert_tile(const ExpertArgs& a, int32_t e, int6
             const int q = tid + kGemmThreads * i;
             const int32_t half = q / kVecPerBlock;       // a constant per i
             dw[i] = __builtin_amdgcn_raw_buffer_load_b128(
-                rw, (int32_t)(half * blk_bytes) + (q % kVecPerBlock) * 16, wso, 0);
+                rw, (int32_t)(half * blk_bytes) + (q % kVecPerBlock) * 16, wso, NTW ? kCachePolicyNt : 0);
         }
     };
     auto load_x = [&](int64_t kt, u32x4 (&dx)[kLoadsX]) {
@@ -326,10 +330,12 @@ __global__ __launch_bounds__(kGemmThreads, 2) void expert_linear_kernel(ExpertAr
         return;
     }
     const int64_t tile = s_sel[1];
-    if (tall)
-        expert_tile<kBTall>(a, e, run_lo + tile * kBTall, r_end, blockIdx.x, s_dyn);
+    if (!tall)
+        expert_tile<kBShort, true>(a, e, run_lo + tile * kBShort, r_end, blockIdx.x, s_dyn);
+    else if (r_end - run_lo <= kBTall)
+        expert_tile<kBTall, true>(a, e, run_lo + tile * kBTall, r_end, blockIdx.x, s_dyn);
     else
-        expert_tile<kBShort>(a, e, run_lo + tile * kBShort, r_end, blockIdx.x, s_dyn);
+        expert_tile<kBTall, false>(a, e, run_lo + tile * kBTall, r_end, blockIdx.x, s_dyn);
 }
 
 // packed[e][nt][kt][r][c] = w[e][nt*128 + r][kt*64 + c]: every 128 x 64 block

@@ -66,6 +66,7 @@ inline hipError_t with_group(int G, int VPT, F&& f) {
 // needs only "stores complete, then flag" on one side and "flag, then loads"
 // on the other, with no L2 write-back or invalidate.
 constexpr int kCachePolicyDevice = 16;   // sc1
+constexpr int kCachePolicyNt = 2;        // nt: streaming, read once
 constexpr int kBufferWord3 = 0x00020000; // raw 32-bit data format (gfx9 family)
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void* row, int64_t bytes) {
