@@ -27,8 +27,18 @@ static size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 // A layout tile holds whole tokens and never straddles a source-rank or chunk
 // boundary: its token count divides gcd(T/R, T/C).  Take the largest such
-// divisor with at most kTileRowsMax rows.
-void make_plan(const ubep_shape& s, Plan* p, int order) {
+// divisor with at most kTileRowsMax rows; with `spread`, where that leaves
+// fewer than kTileTarget tiles, the largest with at most T / kTileTarget
+// tokens instead, if that one still has kTileRowsMin rows.  The workspace is
+// laid out for the spread tiling, which has at least as many tiles, so calls
+// with either tiling share one workspace.
+static int64_t largest_divisor_upto(int64_t g, int64_t cap) {
+    for (int64_t d = g < cap ? g : cap; d > 1; --d)
+        if (g % d == 0) return d;
+    return 1;
+}
+
+void make_plan(const ubep_shape& s, Plan* p, int order, bool spread) {
     p->T = s.T;
     p->H = s.H;
     p->E = s.E;
@@ -43,18 +53,16 @@ void make_plan(const ubep_shape& s, Plan* p, int order) {
     p->tps = s.T / s.R;
     p->tpc = s.T / s.C;
     const int64_t g = gcd64(p->tps, p->tpc);
-    int64_t cap = kTileRowsMax / s.k;
-    if (cap < 1) cap = 1;
-    int64_t tt = 1;
-    for (int64_t d = g < cap ? g : cap; d >= 1; --d) {
-        if (g % d == 0) {
-            tt = d;
-            break;
-        }
-    }
+    const int64_t tt_whole = largest_divisor_upto(g, kTileRowsMax / s.k);
+    const int64_t cap = s.T / kTileTarget < kTileRowsMax / s.k ? s.T / kTileTarget : kTileRowsMax / s.k;
+    int64_t tt_spread = largest_divisor_upto(g, cap);
+    if (tt_spread * s.k < kTileRowsMin) tt_spread = tt_whole;
+    const int64_t tt = spread ? tt_spread : tt_whole;
     p->tile_tokens = tt;
     p->tile_rows = tt * s.k;
     p->n_tiles = s.T / tt;
+    const int64_t n_ws = s.T / tt_spread;      // tiles the workspace is laid out for
+    p->n_tiles_ws = n_ws;
     p->dbits = bits_for(s.R);
     p->ebits = bits_for(s.E);
     p->slots = s.R + s.E;
@@ -68,19 +76,19 @@ void make_plan(const ubep_shape& s, Plan* p, int order) {
     // workspace serves both orders
     size_t off = align_up(kHdrBytes, 256);
     p->off_state = off;
-    off = align_up(off + (size_t)p->n_tiles * p->slots * 8, 256);
+    off = align_up(off + (size_t)n_ws * p->slots * 8, 256);
     p->off_excl = off;
-    off = align_up(off + (size_t)p->n_tiles * s.E * 4, 256);
+    off = align_up(off + (size_t)n_ws * s.E * 4, 256);
     p->off_wbase = off;
-    off = align_up(off + (size_t)p->n_tiles * kLayoutWaves * s.E * 4, 256);
+    off = align_up(off + (size_t)n_ws * kLayoutWaves * s.E * 4, 256);
     p->off_flags = off;
     off = align_up(off + (size_t)s.C * kFlagStride * 4, 256);
     p->off_order = off;
     off = align_up(off + (size_t)s.C * 4, 256);
     p->off_gate_rank = off;
-    off = align_up(off + (size_t)p->n_tiles * s.R * 4, 256);
+    off = align_up(off + (size_t)n_ws * s.R * 4, 256);
     p->off_gate_expert = off;
-    off = align_up(off + (size_t)p->n_tiles * s.E * 4, 256);
+    off = align_up(off + (size_t)n_ws * s.E * 4, 256);
     p->ws_bytes = off;
 }
 
@@ -97,11 +105,11 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 ubep_status hip_status(hipError_t e) { return e == hipSuccess ? UBEP_OK : UBEP_ERR_HIP; }
 
 // Shape check plus the tile-count limit of the layout's workspace.
-ubep_status check_and_plan(const ubep_shape* s, int dtype, Plan* p, int order = 0) {
+ubep_status check_and_plan(const ubep_shape* s, int dtype, Plan* p, int order = 0, bool spread = true) {
     const ubep_status st = ubep_check_shape(s, dtype);
     if (st != UBEP_OK) return st;
-    make_plan(*s, p, order);
-    if (p->n_tiles > kMaxTiles || p->n_tiles * p->slots > kMaxStateWords) return UBEP_ERR_UNSUPPORTED;
+    make_plan(*s, p, order, spread);
+    if (p->n_tiles_ws > kMaxTiles || p->n_tiles_ws * p->slots > kMaxStateWords) return UBEP_ERR_UNSUPPORTED;
     return UBEP_OK;
 }
 
@@ -239,7 +247,9 @@ ubep_status ubep_layout_dispatch(const ubep_shape* s, const int32_t* topk_idx, c
                                  int32_t* recv_src, void* recv, void* ws, size_t ws_bytes,
                                  hipStream_t stream) {
     Plan p;
-    const ubep_status st = check_and_plan(s, UBEP_BF16, &p);
+    // the largest tiles, so the fewest layout workgroups: with the spread
+    // tiling this kernel was slower on a 4096-token decode step
+    const ubep_status st = check_and_plan(s, UBEP_BF16, &p, 0, false);
     if (st != UBEP_OK) return st;
     if (!topk_idx || !x || !pos || !expert_count || !rank_count || !recv_offset || !send_offset ||
         !recv || !ws)
@@ -284,7 +294,9 @@ ubep_status ubep_gate_layout(const ubep_gate_shape* g, const ubep_shape* s, cons
     ubep_status st = check_gate(g, logits, topk_idx, topk_w);
     if (st != UBEP_OK) return st;
     Plan p;
-    st = check_and_plan(s, UBEP_BF16, &p);
+    // the largest tiles: the per-tile counts that the gate writes, and that
+    // the counted layout's last workgroup clears, grow with the tile count
+    st = check_and_plan(s, UBEP_BF16, &p, 0, false);
     if (st != UBEP_OK) return st;
     if (g->T != s->T || g->E != s->E || g->k != s->k) return UBEP_ERR_INVALID_ARG;
     if (!pos || !expert_count || !rank_count || !recv_offset || !send_offset || !ws)

@@ -19,10 +19,15 @@ constexpr int kExpertMaxE = 1024;        // experts of ubep_expert_linear
 constexpr int64_t kExpertMaxRowTiles = 65535;   // row tiles (grid.y) of ubep_expert_linear
 
 // Layout kernel: 8 waves per workgroup, tiles of whole tokens with at most
-// kTileRowsMax rows.
+// kTileRowsMax rows.  A workgroup ranks its tile's rows one 64-row step after
+// another, so tiles are also kept small enough for about kTileTarget of them
+// (the ranking then runs on that many CUs at once), but not below
+// kTileRowsMin rows.
 constexpr int kLayoutThreads = 512;
 constexpr int kLayoutWaves = 8;
 constexpr int64_t kTileRowsMax = 4096;
+constexpr int64_t kTileTarget = 128;
+constexpr int64_t kTileRowsMin = 256;
 constexpr int64_t kLdsBytesPerCu = 160 * 1024;
 
 // Workspace header: 32-bit counters, each on its own 128-byte line.
@@ -85,14 +90,14 @@ struct Plan {
     int32_t gather;        // 1: prefixes and totals by gathering all tiles' counts
     // workspace byte offsets
     int32_t slots;         // look-back digits per tile: R ranks, then E experts
-    size_t off_state;      // uint64 [n_tiles][R+E]  look-back state
-    size_t off_excl;       // int32  [n_tiles][K]    rows with key q in earlier tiles (sized for K = E)
-    size_t off_wbase;      // int32  [n_tiles][8][K] rows with key q in earlier waves of the tile
+    size_t off_state;      // uint64 [n_tiles_ws][R+E]  look-back state
+    size_t off_excl;       // int32  [n_tiles_ws][K]    rows with key q in earlier tiles (sized for K = E)
+    size_t off_wbase;      // int32  [n_tiles_ws][8][K] rows with key q in earlier waves of the tile
     size_t off_flags;      // uint32 [C][kFlagStride] chunk ready flags
     size_t ws_bytes;
     size_t off_order;      // int32  [C] chunk order computed on the device (LPT policy)
-    size_t off_gate_rank;  // int32  [n_tiles][R] rows per (tile, rank) counted by the gate
-    size_t off_gate_expert; // int32 [n_tiles][E] rows per (tile, expert) counted by the gate
+    size_t off_gate_rank;  // int32  [n_tiles_ws][R] rows per (tile, rank) counted by the gate
+    size_t off_gate_expert; // int32 [n_tiles_ws][E] rows per (tile, expert) counted by the gate
     // Position keys (last, so that the fields the rank-order kernels read keep
     // their places).  Rank order: rows sort by (rank, token, slot), one key
     // per rank.  Expert order: rows sort by (expert, token, slot), one key per
@@ -103,10 +108,12 @@ struct Plan {
     uint32_t key_magic;    // epr_magic (rank order) or 0 (expert order: key = e)
     int32_t kbits;         // bits to hold a key
     int32_t kcol;          // state digit of key 0: 0 (rank digits) or R (expert digits)
+    int64_t n_tiles_ws;    // tiles the workspace arrays are sized for (>= n_tiles)
 };
 
 // Host: fill `p` for a shape that passed validation; order 0 (rank order)
-// or 1 (expert order).  The workspace layout does not depend on the order.
-void make_plan(const ubep_shape& s, Plan* p, int order = 0);
+// or 1 (expert order); spread: the tiling with about kTileTarget tiles, else
+// the one with the largest tiles.  The workspace layout depends on neither.
+void make_plan(const ubep_shape& s, Plan* p, int order = 0, bool spread = true);
 
 }  // namespace ubep

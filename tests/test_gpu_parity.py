@@ -42,6 +42,8 @@ MEDIUM = [
     dict(T=255, H=7168, E=40, k=8, R=5, C=3, routing="zipf", seed=10),
     dict(T=512, H=7168, E=256, k=8, R=32, C=2, routing="topk", seed=11),
     dict(T=384, H=4096, E=128, k=8, R=16, C=1, routing="topk", seed=12),
+    # 42000 rows, odd k: 240 tiles of 175 rows (not a multiple of 64)
+    dict(T=6000, H=32, E=56, k=7, R=8, C=3, routing="zipf", seed=13),
 ]
 
 
@@ -88,17 +90,17 @@ def test_medium_shapes_bit_exact(spec, fused):
 
 
 # worker caps that make layout workgroups take several tiles each: gather mode
-# (few tiles; 16 tiles on 2 workers is exactly the per-worker claim limit) and
-# look-back mode (256 tiles x 256 ranks)
+# (few tiles; 32 tiles on 4 workers is exactly the per-worker claim limit,
+# which the cap of 1 is raised to) and look-back mode (256 tiles x 256 ranks)
 CAPPED = [
     (dict(T=1024, H=64, E=64, k=8, R=16, C=4, routing="zipf", seed=21), 1),
-    (dict(T=1024, H=64, E=64, k=8, R=16, C=4, routing="zipf", seed=21), 3),
+    (dict(T=1024, H=64, E=64, k=8, R=16, C=4, routing="zipf", seed=21), 5),
     (dict(T=16384, H=16, E=256, k=2, R=256, C=4, routing="topk", seed=22), 5),
 ]
 
 
 @pytest.mark.parametrize("fused", [False, True], ids=["separate", "fused"])
-@pytest.mark.parametrize("spec,cap", CAPPED, ids=["gather-cap1", "gather-cap3", "lookback-cap5"])
+@pytest.mark.parametrize("spec,cap", CAPPED, ids=["gather-cap1", "gather-cap5", "lookback-cap5"])
 def test_layout_workers_taking_several_tiles(spec, cap, fused):
     ubep.ubep_set_layout_workers(cap)
     try:

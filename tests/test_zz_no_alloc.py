@@ -51,7 +51,7 @@ def _same(a, b, C):
 
 def test_noalloc_layout_matches_workspace_layout_on_consecutive_calls():
     status = torch.zeros(1, dtype=torch.int32, device="cuda")
-    cases = [make_config("dsv3_decode_zipf_T4096_H7168_E256_k8_R32"),          # 32 tiles
+    cases = [make_config("dsv3_decode_zipf_T4096_H7168_E256_k8_R32"),          # 128 tiles
              custom(T=1024, H=8, E=64, k=8, R=16, C=4, routing="zipf", seed=71),  # smaller
              custom(T=96, H=8, E=12, k=3, R=6, C=2, routing="topk", seed=72),     # one workgroup
              make_config("prefill_grouped_zipf_T65536_H7168_E256_k8_R64_C16")]    # 128 tiles
