@@ -67,7 +67,7 @@ def algorithmic_bytes(s: dict, fp8: bool, gate: bool = False, expert_w_bytes: in
 KERNEL_SOURCES = {
     "combine": ["combine.hip", "rows.h", "launch.h", "device_common.h", "plan.h"],
     "dispatch": ["dispatch.hip", "rows.h", "launch.h", "device_common.h", "plan.h"],
-    "layout": ["layout.hip", "layout_worker.h", "launch.h", "device_common.h", "plan.h"],
+    "layout": ["layout.hip", "layout_worker.h", "launch.h", "device_common.h", "plan.h", "api.hip"],
     "expert": ["expert.hip", "rows.h", "launch.h", "device_common.h", "plan.h"],
 }
 
@@ -461,10 +461,11 @@ def measure(name: str, args, hev) -> dict:
 
 def stream_ceilings(sd: dict, reps: int = 10) -> dict:
     """Sequential-stream rates in this run, sized like the step's kernels
-    (ubep_stream_probe; back to back, median of reps): a read stream and a
-    write stream of the receive rows' bytes, and the combine's and the
-    dispatch's byte mixes (eight 16-byte vectors read per vector written, and
-    the reverse)."""
+    (ubep_stream_probe; reps launches back to back between two events, no
+    event between them, median of 3 such passes): a read stream and a write
+    stream of the receive rows' bytes, and the combine's and the dispatch's
+    byte mixes (eight 16-byte vectors read per vector written, and the
+    reverse)."""
     import torch
 
     import combine_top_route_amd as ubep
@@ -479,14 +480,17 @@ def stream_ceilings(sd: dict, reps: int = 10) -> dict:
     stream = torch.cuda.current_stream()
     for key, (src, dst, fi, fo) in cases.items():
         ubep.ubep_stream_probe(src, dst, n, fi, fo, stream)
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        passes = []
+        for _ in range(3):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for i in range(reps):
+                ubep.ubep_stream_probe(src, dst, n, fi, fo, stream)
+            e1.record(stream)
+            passes.append((e0, e1))
         torch.cuda.synchronize()
-        ev[0].record(stream)
-        for i in range(reps):
-            ubep.ubep_stream_probe(src, dst, n, fi, fo, stream)
-            ev[i + 1].record(stream)
-        torch.cuda.synchronize()
-        us = statistics.median(ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(reps))
+        us = statistics.median(a.elapsed_time(b) * 1e3 / reps for a, b in passes)
         nbytes = 16 * n * (fi + fo)
         out[key] = {"bytes": nbytes, "us": round(us, 2), "GBs": round(nbytes / us / 1e3, 1)}
     del big, small
@@ -692,8 +696,9 @@ def main(argv=None):
         line["stream_ceilings"] = {
             **ceilings,
             "note": ("sequential streams of the receive rows' size in this run (ubep_stream_probe, "
-                     "warm, median of 10): read only, write only, and the combine's (8 read : 1 "
-                     "written) and dispatch's (1 : 8) byte mixes"),
+                     "one 16-byte vector per thread over the whole range; warm, 10 launches back "
+                     "to back, median of 3 passes): read only, write only, and the combine's (8 "
+                     "read : 1 written) and dispatch's (1 : 8) byte mixes"),
             "kernels": rel}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
