@@ -1,6 +1,7 @@
 """GPU parity on seeded random shapes: the layout in both key orders (every
 output, bit-exact against the oracle), and dispatch + combine (whole outputs)
-with the separate calls and with the fused layout + dispatch launch.
+with the separate calls, the fused layout + dispatch launch, the chunk
+pipeline and the sentinel pipeline.
 
 The shapes are drawn once from a fixed seed so that every run checks the same
 cases.  They spread over what picks the layout's kernel and tiling: rows from
@@ -16,6 +17,7 @@ import torch
 
 import combine_top_route_amd as ubep
 import oracle
+from combine_top_route_amd.buffers import run_path
 from workloads import custom
 from gpu_helpers import LAYOUT_KEYS, assert_layout_equal, device_status, say, to_np, upload
 
@@ -107,3 +109,35 @@ def test_random_shape_layouts_and_path(spec):
     got = {k: to_np(getattr(b, k)) for k in LAYOUT_KEYS}
     got["expert_offset"] = to_np(eoff)
     _grouped_equal(got, oracle.layout_grouped(w.topk_idx, s.E, s.R, C), C)
+
+
+@pytest.mark.parametrize("spec", SHAPES[::2], ids=IDS[::2])
+def test_random_shape_pipelines(spec):
+    """The chunk pipeline (index order and the device's LPT order) and the
+    sentinel pipeline against the oracle's dispatch + combine, whole outputs."""
+    w = custom(weights="softmax", **spec)
+    s = w.shape
+    say(f"random shape pipelines {spec}")
+    b = upload(w)
+    ref = oracle.layout(w.topk_idx, s.E, s.R, s.C)
+    recv = oracle.dispatch_bf16(w.x, ref["pos"])
+    out = oracle.combine(recv, ref["pos"], w.topk_w)
+    for order in (None, "lpt"):
+        b.out.zero_()
+        b.recv.zero_()
+        run_path(b, chunked=True, chunk_order=order)
+        torch.cuda.synchronize()
+        assert device_status(b) == ubep.OK, order
+        np.testing.assert_array_equal(to_np(b.recv), recv, err_msg=str(order))
+        np.testing.assert_array_equal(to_np(b.out), out, err_msg=str(order))
+    # sentinel pipeline: every receive row's first 16 bytes start as the
+    # sentinel and hold it again after the call
+    ubep.ubep_recv_sentinel_init(b.recv, s.T * s.k, s.H)
+    b.out.zero_()
+    ubep.ubep_dispatch_combine_sentinel(b.shape, b.x, b.pos, b.topk_w, b.recv, b.out, b.ws)
+    torch.cuda.synchronize()
+    assert device_status(b) == ubep.OK
+    np.testing.assert_array_equal(to_np(b.out), out)
+    got = to_np(b.recv)
+    assert np.all(got[:, :8] == 0xFFFF)
+    np.testing.assert_array_equal(got[:, 8:], recv[:, 8:])
