@@ -141,3 +141,27 @@ def test_random_shape_pipelines(spec):
     got = to_np(b.recv)
     assert np.all(got[:, :8] == 0xFFFF)
     np.testing.assert_array_equal(got[:, 8:], recv[:, 8:])
+
+
+FP8_SHAPES = [dict(s, H=128 * (1 + i % 3), payload="fp8") for i, s in enumerate(SHAPES[1::4])]
+
+
+@pytest.mark.parametrize("spec", FP8_SHAPES,
+                         ids=[f"T{s['T']}E{s['E']}k{s['k']}R{s['R']}H{s['H']}" for s in FP8_SHAPES])
+def test_random_shape_fp8_path(spec):
+    """fp8 payload: codes, scales, the identity expert's bf16 rows and the
+    combined output, whole, against the oracle."""
+    w = custom(weights="softmax", **spec)
+    s = w.shape
+    say(f"random shape fp8 {spec}")
+    b = upload(w)
+    run_path(b)
+    torch.cuda.synchronize()
+    assert device_status(b) == ubep.OK
+    ref = oracle.layout(w.topk_idx, s.E, s.R, s.C)
+    q, sc = oracle.dispatch_fp8(w.x, ref["pos"])
+    np.testing.assert_array_equal(to_np(b.recv), q)
+    np.testing.assert_array_equal(to_np(b.recv_scale), sc)
+    y = oracle.identity_fp8(q, sc)
+    np.testing.assert_array_equal(to_np(b.y), y)
+    np.testing.assert_array_equal(to_np(b.out), oracle.combine(y, ref["pos"], w.topk_w))
