@@ -29,7 +29,8 @@ static size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 // boundary: its token count divides gcd(T/R, T/C).  Take the largest such
 // divisor with at most kTileRowsMax rows; with `spread`, where that leaves
 // fewer than kTileTarget tiles, the largest with at most T / kTileTarget
-// tokens instead, if that one still has kTileRowsMin rows.  The workspace is
+// tokens instead, if that one still has kTileRowsMin rows and makes at most
+// 2 * kTileTarget tiles.  The workspace is
 // laid out for the spread tiling, which has at least as many tiles, so calls
 // with either tiling share one workspace.
 static int64_t largest_divisor_upto(int64_t g, int64_t cap) {
@@ -56,7 +57,9 @@ void make_plan(const ubep_shape& s, Plan* p, int order, bool spread) {
     const int64_t tt_whole = largest_divisor_upto(g, kTileRowsMax / s.k);
     const int64_t cap = s.T / kTileTarget < kTileRowsMax / s.k ? s.T / kTileTarget : kTileRowsMax / s.k;
     int64_t tt_spread = largest_divisor_upto(g, cap);
-    if (tt_spread * s.k < kTileRowsMin) tt_spread = tt_whole;
+    // keep the largest tiles when the divisors of g allow no spread tiling
+    // of at least kTileRowsMin rows and at most 2 * kTileTarget tiles
+    if (tt_spread * s.k < kTileRowsMin || s.T / tt_spread > 2 * kTileTarget) tt_spread = tt_whole;
     const int64_t tt = spread ? tt_spread : tt_whole;
     p->tile_tokens = tt;
     p->tile_rows = tt * s.k;
