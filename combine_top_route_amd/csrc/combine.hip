@@ -28,10 +28,23 @@ __global__ __launch_bounds__(kCombineBlock) void combine_kernel(const u32x4* __r
     combine_row<G, VPT, kSlotBatch>(y, pos, w, out, t, k, nvec, n_rows, threadIdx.x % G, status);
 }
 
+// Two waves per token where the shared rule gives one wave eight vectors per
+// thread (449 to 512 vectors, H = 4096 among them): two waves of four
+// vectors each took 208 us against 225 us for the combine of a 16384-token
+// chunk at H = 4096.  (Rows of 256 vectors stay at one wave: two waves of two
+// vectors each were 15 % slower on 65536 tokens.)
+static void pick_combine_group(int64_t nvec, int* G, int* VPT) {
+    pick_group(nvec, G, VPT);
+    if (*G == 64 && *VPT == kVptCap) {
+        *G = 128;
+        *VPT = (int)((nvec + 127) / 128);
+    }
+}
+
 hipError_t launch_combine(const Plan& p, const void* y, const int32_t* pos, const float* topk_w,
                           void* out, uint32_t* status, hipStream_t stream) {
     int G, VPT;
-    pick_group(p.H / 8, &G, &VPT);
+    pick_combine_group(p.H / 8, &G, &VPT);
     auto go = [&]<int GG, int VV>() -> hipError_t {
         constexpr int TPB = kCombineBlock / GG;
         const int64_t blocks = (p.T + TPB - 1) / TPB;

@@ -37,8 +37,8 @@ MEDIUM = [
     dict(T=64, H=8, E=2, k=2, R=1, C=1, routing="topk", seed=7),            # one rank, tiny H
     # the row kernels' instantiations that the full-size workloads run:
     # H = 7168 (groups of 128 threads, 7 vectors each; decode and large
-    # prefill) with a ragged last block of one token, and H = 4096 (groups of
-    # 64 threads, 8 vectors each; the combine of the fp8 prefill)
+    # prefill) with a ragged last block of one token, and H = 4096 (combine
+    # groups of 128 threads, 4 vectors each; the combine of the fp8 prefill)
     dict(T=255, H=7168, E=40, k=8, R=5, C=3, routing="zipf", seed=10),
     dict(T=512, H=7168, E=256, k=8, R=32, C=2, routing="topk", seed=11),
     dict(T=384, H=4096, E=128, k=8, R=16, C=1, routing="topk", seed=12),
