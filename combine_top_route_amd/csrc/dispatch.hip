@@ -9,7 +9,12 @@
 
 namespace ubep {
 
-constexpr int kRowBlock = 256;
+// 512 threads: 4 bf16 tokens (H = 7168) or 2 fp8 tokens (H = 4096) per
+// workgroup; against 256, 1 % faster at the decode, the 65536-token prefill
+// and the fp8 Qwen3 prefill shapes (75.0 / 1597 / 104.6 us against 75.8 /
+// 1617 / 106.1 us).  A group never exceeds 256 threads, so a workgroup always
+// holds whole groups.
+constexpr int kRowBlock = 512;
 
 // Blocks from nt_from on (the last ones to start) write their rows with
 // non-temporal stores: the rows written last would otherwise still sit dirty
