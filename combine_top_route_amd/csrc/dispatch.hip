@@ -19,9 +19,11 @@ constexpr int kRowBlock = 512;
 // Blocks from nt_from on (the last ones to start) write their rows with
 // non-temporal stores: the rows written last would otherwise still sit dirty
 // in the L2s when the kernel ends, and the next kernel's loads would pay for
-// writing them back.  The tail is about twice the L2s' 32 MB, written while
-// the grid drains and HBM has room.
-constexpr int64_t kNtTailBytes = 64ll << 20;
+// writing them back.  The tail is 128 MB, four times the L2s' 32 MB, written
+// while the grid drains and HBM has room: on the 4096-token decode step, a
+// step of dispatch then combine took 178.2 us from a cold cache with it,
+// against 182.0 (64 MB), 180.1 (192 MB) and 185.9 us (256 MB).
+constexpr int64_t kNtTailBytes = 128ll << 20;
 
 template <int G, int VPT>
 __global__ __launch_bounds__(kRowBlock) void dispatch_bf16_kernel(const u32x4* __restrict__ x,
