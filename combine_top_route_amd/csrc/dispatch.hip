@@ -19,13 +19,23 @@ constexpr int kRowBlock = 512;
 // Blocks from nt_from on (the last ones to start) write their rows with
 // non-temporal stores: the rows written last would otherwise still sit dirty
 // in the L2s when the kernel ends, and the next kernel's loads would pay for
-// writing them back.  The tail is 128 MB, four times the L2s' 32 MB, written
-// while the grid drains and HBM has room: on the 4096-token decode step, a
-// step of dispatch then combine took 178.2 us from a cold cache with it,
-// against 182.0 (64 MB), 180.1 (192 MB) and 185.9 us (256 MB).
-constexpr int64_t kNtTailBytes = 128ll << 20;
+// writing them back.  The tail is 160 MB, five times the L2s' 32 MB, written
+// while the grid drains and HBM has room.  On the 4096-token decode step (a
+// step of layout, dispatch and combine from a cold cache) 128 MB took 178.2
+// us against 182.0 (64 MB), 180.1 (192 MB) and 185.9 us (256 MB); with x
+// read non-temporally as well, 160 MB took 176.5 us against 176.8 (128 MB)
+// and 179.1 us (192 MB).
+constexpr int64_t kNtTailBytes = 160ll << 20;
 
-template <int G, int VPT>
+// Up to this many bytes of receive rows, x is read with non-temporal loads
+// too: on the decode step that, with the tail above, left the combine that
+// follows fewer lines to evict (step 177.5 -> 176.5 us cold, Zipf warm 184.0
+// -> 180.0 us), while from 32768 tokens of H = 7168 (3.8 GB of rows) it made
+// the dispatch itself 1.5 % slower; at 16384 tokens (1.9 GB) it changed
+// nothing.
+constexpr int64_t kNtxMaxBytes = 2ll << 30;
+
+template <int G, int VPT, bool NTX>
 __global__ __launch_bounds__(kRowBlock) void dispatch_bf16_kernel(const u32x4* __restrict__ x,
                                                                   const int32_t* __restrict__ pos,
                                                                   u32x4* __restrict__ recv,
@@ -37,9 +47,11 @@ __global__ __launch_bounds__(kRowBlock) void dispatch_bf16_kernel(const u32x4* _
     const int64_t t = (int64_t)blk * TPB + threadIdx.x / G;
     if (t >= T) return;
     if (blk >= nt_from)
-        dispatch_row_bf16<G, VPT, true>(x, pos, recv, t, k, nvec, n_rows, threadIdx.x % G, status);
+        dispatch_row_bf16<G, VPT, true, false, false, NTX>(x, pos, recv, t, k, nvec, n_rows,
+                                                           threadIdx.x % G, status);
     else
-        dispatch_row_bf16<G, VPT, false>(x, pos, recv, t, k, nvec, n_rows, threadIdx.x % G, status);
+        dispatch_row_bf16<G, VPT, false, false, false, NTX>(x, pos, recv, t, k, nvec, n_rows,
+                                                            threadIdx.x % G, status);
 }
 
 template <int G>
@@ -64,9 +76,10 @@ hipError_t launch_dispatch_bf16(const Plan& p, const void* x, const int32_t* pos
     auto go = [&]<int GG, int VV>() -> hipError_t {
         constexpr int TPB = kRowBlock / GG;
         const int64_t blocks = (p.T + TPB - 1) / TPB;
+        const auto kernel = p.rows * p.H * 2 <= kNtxMaxBytes ? dispatch_bf16_kernel<GG, VV, true>
+                                                             : dispatch_bf16_kernel<GG, VV, false>;
         int64_t n_static = 0;
-        const hipError_t e = resident_blocks(
-            reinterpret_cast<const void*>(dispatch_bf16_kernel<GG, VV>), kRowBlock, 0, &n_static);
+        const hipError_t e = resident_blocks(reinterpret_cast<const void*>(kernel), kRowBlock, 0, &n_static);
         if (e != hipSuccess) return e;
         // start-order tickets only when later workgroups are many more than
         // the first resident wave (long grids drift apart across XCDs); with
@@ -75,7 +88,7 @@ hipError_t launch_dispatch_bf16(const Plan& p, const void* x, const int32_t* pos
         const int64_t block_bytes = (int64_t)TPB * p.k * p.H * 2;   // receive rows a block writes
         const int64_t nt_blocks = (kNtTailBytes + block_bytes - 1) / block_bytes;
         const int64_t nt_from = blocks > nt_blocks ? blocks - nt_blocks : 0;
-        return launch_kernel(dispatch_bf16_kernel<GG, VV>, dim3((unsigned)blocks),
+        return launch_kernel(kernel, dim3((unsigned)blocks),
                              dim3(kRowBlock), 0, stream, static_cast<const u32x4*>(x), pos,
                              static_cast<u32x4*>(recv), p.T, p.k, p.H / 8, p.rows, status,
                              (uint32_t)n_static, (uint32_t)nt_from);

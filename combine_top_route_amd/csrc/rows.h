@@ -110,8 +110,9 @@ __device__ __forceinline__ bool row_ok(int32_t q, int64_t n_rows) {
 
 // recv[pos[t][j]] = x[t] for j = 0..k-1 (bf16 bit copy, no relay buffer).
 // COH: write the rows with device-coherent stores (see above).  SKIP0: leave
-// each row's first 16-byte unit unwritten (the caller stores it last).
-template <int G, int VPT, bool NT, bool COH = false, bool SKIP0 = false>
+// each row's first 16-byte unit unwritten (the caller stores it last).  NTX:
+// read x with non-temporal loads.
+template <int G, int VPT, bool NT, bool COH = false, bool SKIP0 = false, bool NTX = false>
 __device__ __forceinline__ void dispatch_row_bf16(const u32x4* __restrict__ x,
                                                   const int32_t* __restrict__ pos,
                                                   u32x4* __restrict__ recv, int64_t t, int32_t k,
@@ -125,7 +126,7 @@ __device__ __forceinline__ void dispatch_row_bf16(const u32x4* __restrict__ x,
 #pragma unroll
         for (int i = 0; i < VPT; ++i) {
             const int64_t v = v0 + gtid + (int64_t)i * G;
-            if (v < nvec) buf[i] = xr[v];
+            if (v < nvec) buf[i] = NTX ? __builtin_nontemporal_load(xr + v) : xr[v];
         }
         for (int32_t j = 0; j < k; ++j) {
             const int32_t q = pr[j];
