@@ -127,10 +127,13 @@ ubep_status ubep_workspace_init(void *ws, size_t ws_bytes, hipStream_t stream);
  *   recv_src[T*k]      inverse of pos: recv_src[pos[t][j]] = t*k + j (may be NULL).
  * A topk_idx entry outside [0, E) sets UBEP_ERR_BAD_EXPERT_ID in the device
  * status; the outputs are then unspecified but every pos stays in [0, T*k).
- * One kernel on `stream`: persistent workgroups over tiles of whole tokens
+ * One kernel on `stream`.  Rows are cut into tiles of whole tokens (about
+ * 128 tiles where each keeps at least 256 rows, else the largest up to 4096
+ * rows).  Up to 4096 rows: one workgroup.  Up to 32768 rows (E <= 1024, at
+ * most 256 tiles): one workgroup per tile that counts every id itself, so no
+ * value crosses workgroups.  Beyond: persistent workgroups over the tiles
  * that publish per-tile counts in the workspace and read each other's (all
- * of them at once for up to 512 tiles, a decoupled look-back beyond), or one
- * workgroup for problems of at most 4096 rows. */
+ * of them at once for up to 512 tiles, a decoupled look-back beyond). */
 ubep_status ubep_layout(const ubep_shape *shape /*host*/, const int32_t *topk_idx,
                         int32_t *pos, int32_t *expert_count, int32_t *rank_count,
                         int32_t *recv_offset, int32_t *send_offset, int32_t *chunk_offset,
