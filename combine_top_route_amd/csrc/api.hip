@@ -30,9 +30,9 @@ static size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 // divisor with at most kTileRowsMax rows; with `spread`, where that leaves
 // fewer than kTileTarget tiles, the largest with at most T / kTileTarget
 // tokens instead, if that one still has kTileRowsMin rows and makes at most
-// 2 * kTileTarget tiles.  The workspace is
-// laid out for the spread tiling, which has at least as many tiles, so calls
-// with either tiling share one workspace.
+// 2 * kTileTarget tiles.  The workspace is laid out for the spread tiling,
+// which has at least as many tiles, so calls with either tiling share one
+// workspace.
 static int64_t largest_divisor_upto(int64_t g, int64_t cap) {
     for (int64_t d = g < cap ? g : cap; d > 1; --d)
         if (g % d == 0) return d;
