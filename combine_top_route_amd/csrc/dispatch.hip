@@ -16,24 +16,8 @@ namespace ubep {
 // holds whole groups.
 constexpr int kRowBlock = 512;
 
-// Blocks from nt_from on (the last ones to start) write their rows with
-// non-temporal stores: the rows written last would otherwise still sit dirty
-// in the L2s when the kernel ends, and the next kernel's loads would pay for
-// writing them back.  The tail is 160 MB, five times the L2s' 32 MB, written
-// while the grid drains and HBM has room.  On the 4096-token decode step (a
-// step of layout, dispatch and combine from a cold cache) 128 MB took 178.2
-// us against 182.0 (64 MB), 180.1 (192 MB) and 185.9 us (256 MB); with x
-// read non-temporally as well, 160 MB took 176.5 us against 176.8 (128 MB)
-// and 179.1 us (192 MB).
-constexpr int64_t kNtTailBytes = 160ll << 20;
-
-// Up to this many bytes of receive rows, x is read with non-temporal loads
-// too: on the decode step that, with the tail above, left the combine that
-// follows fewer lines to evict (step 177.5 -> 176.5 us cold, Zipf warm 184.0
-// -> 180.0 us), while from 32768 tokens of H = 7168 (3.8 GB of rows) it made
-// the dispatch itself 1.5 % slower; at 16384 tokens (1.9 GB) it changed
-// nothing.
-constexpr int64_t kNtxMaxBytes = 2ll << 30;
+// kNtTailBytes and kNtxMaxBytes (rows.h) set the non-temporal tail and the
+// non-temporal reads of x.
 
 template <int G, int VPT, bool NTX>
 __global__ __launch_bounds__(kRowBlock) void dispatch_bf16_kernel(const u32x4* __restrict__ x,

@@ -31,12 +31,15 @@ constexpr int kFusedWaves = kFusedThreads / 64;
 constexpr int64_t kFusedLdsMax = 24 * 1024;     // keep data workers at full occupancy
 constexpr int kFusedWindow = 32;                 // look-back window of the layout workers
 
-template <int G, int VPT, int LR>
+// NTX: x read with non-temporal loads; row blocks from nt_from on store
+// non-temporally (the dispatch kernel's policy, rows.h).
+template <int G, int VPT, int LR, bool NTX>
 __global__ __launch_bounds__(kFusedThreads) void layout_dispatch_kernel(LayoutArgs la,
                                                                        const u32x4* __restrict__ x,
                                                                        u32x4* __restrict__ recv,
                                                                        uint32_t n_workers,
-                                                                       uint32_t n_static) {
+                                                                       uint32_t n_static,
+                                                                       uint32_t nt_from) {
     extern __shared__ int32_t dyn_lds[];
     __shared__ uint32_t s_role;
     __shared__ int32_t s_pos[kFusedThreads / 64 * kMaxK];
@@ -77,7 +80,7 @@ __global__ __launch_bounds__(kFusedThreads) void layout_dispatch_kernel(LayoutAr
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
         const int64_t v = gtid + (int64_t)i * G;
-        if (live && v < nvec) buf[i] = xr[v];
+        if (live && v < nvec) buf[i] = NTX ? __builtin_nontemporal_load(xr + v) : xr[v];
     }
     if (tid == 0) {
         const uint64_t t0 = now_ticks();
@@ -100,7 +103,7 @@ __global__ __launch_bounds__(kFusedThreads) void layout_dispatch_kernel(LayoutAr
 #pragma unroll
                 for (int i = 0; i < VPT; ++i) {
                     const int64_t v = v0 + gtid + (int64_t)i * G;
-                    if (v < nvec) buf[i] = xr[v];
+                    if (v < nvec) buf[i] = NTX ? __builtin_nontemporal_load(xr + v) : xr[v];
                 }
             }
             for (int32_t j = 0; j < p.k; ++j) {
@@ -113,7 +116,10 @@ __global__ __launch_bounds__(kFusedThreads) void layout_dispatch_kernel(LayoutAr
 #pragma unroll
                 for (int i = 0; i < VPT; ++i) {
                     const int64_t v = v0 + gtid + (int64_t)i * G;
-                    if (v < nvec) dst[v] = buf[i];
+                    if (v < nvec) {
+                        if (blk >= nt_from) __builtin_nontemporal_store(buf[i], dst + v);
+                        else dst[v] = buf[i];
+                    }
                 }
             }
         }
@@ -170,6 +176,10 @@ hipError_t launch_layout_dispatch(const Plan& p, const int32_t* idx, const void*
         constexpr int TPB = kFusedThreads / GG;
         int64_t grid = (p.T + TPB - 1) / TPB;     // one block of tokens per workgroup
         if (grid < (int64_t)n_workers) grid = n_workers;
+        const int64_t data_blocks = (p.T + TPB - 1) / TPB;
+        const int64_t block_bytes = (int64_t)TPB * p.k * p.H * 2;   // receive rows a block writes
+        const int64_t nt_blocks = (kNtTailBytes + block_bytes - 1) / block_bytes;
+        const int64_t nt_from = data_blocks > nt_blocks ? data_blocks - nt_blocks : 0;
         const auto one = [&](auto kernel) -> hipError_t {
             int64_t n_static = 0;
             const hipError_t err = resident_blocks(reinterpret_cast<const void*>(kernel), kFusedThreads,
@@ -178,11 +188,14 @@ hipError_t launch_layout_dispatch(const Plan& p, const int32_t* idx, const void*
             if (n_static > grid) n_static = grid;
             return launch_kernel(kernel, dim3((unsigned)grid), dim3(kFusedThreads), lds, stream, a,
                                  static_cast<const u32x4*>(x), static_cast<u32x4*>(recv), n_workers,
-                                 (uint32_t)n_static);
+                                 (uint32_t)n_static, (uint32_t)nt_from);
         };
-        if (lane_need <= 4) return one(layout_dispatch_kernel<GG, VV, 4>);
-        if (lane_need <= 8) return one(layout_dispatch_kernel<GG, VV, 8>);
-        return one(layout_dispatch_kernel<GG, VV, 16>);
+        const bool ntx = p.rows * p.H * 2 <= kNtxMaxBytes;
+        if (lane_need <= 4)
+            return ntx ? one(layout_dispatch_kernel<GG, VV, 4, true>) : one(layout_dispatch_kernel<GG, VV, 4, false>);
+        if (lane_need <= 8)
+            return ntx ? one(layout_dispatch_kernel<GG, VV, 8, true>) : one(layout_dispatch_kernel<GG, VV, 8, false>);
+        return ntx ? one(layout_dispatch_kernel<GG, VV, 16, true>) : one(layout_dispatch_kernel<GG, VV, 16, false>);
     };
     return with_group(G, VPT, go);
 }
