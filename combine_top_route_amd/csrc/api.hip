@@ -32,14 +32,14 @@ static size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 // tokens instead, if that one still has kTileRowsMin rows and makes at most
 // 2 * kTileTarget tiles.  The workspace is laid out for the spread tiling,
 // which has at least as many tiles, so calls with either tiling share one
-// workspace.
+// workspace (ws_spread false: for the tiling in use only).
 static int64_t largest_divisor_upto(int64_t g, int64_t cap) {
     for (int64_t d = g < cap ? g : cap; d > 1; --d)
         if (g % d == 0) return d;
     return 1;
 }
 
-void make_plan(const ubep_shape& s, Plan* p, int order, bool spread) {
+void make_plan(const ubep_shape& s, Plan* p, int order, bool spread, bool ws_spread) {
     p->T = s.T;
     p->H = s.H;
     p->E = s.E;
@@ -64,7 +64,7 @@ void make_plan(const ubep_shape& s, Plan* p, int order, bool spread) {
     p->tile_tokens = tt;
     p->tile_rows = tt * s.k;
     p->n_tiles = s.T / tt;
-    const int64_t n_ws = s.T / tt_spread;      // tiles the workspace is laid out for
+    const int64_t n_ws = s.T / (ws_spread ? tt_spread : tt);   // tiles the workspace is laid out for
     p->n_tiles_ws = n_ws;
     p->dbits = bits_for(s.R);
     p->ebits = bits_for(s.E);
@@ -204,7 +204,13 @@ ubep_status ubep_layout_noalloc(const ubep_shape* s, const int32_t* topk_idx, in
     if (!topk_idx || !pos || !expert_count || !rank_count || !recv_offset || !send_offset || !status)
         return UBEP_ERR_INVALID_ARG;
     if (!aligned(status, 4)) return UBEP_ERR_INVALID_ARG;
-    if (p.ws_bytes > kScratchBytes) return UBEP_ERR_UNSUPPORTED;
+    if (p.ws_bytes > kScratchBytes) {
+        // the spread tiling's workspace does not fit the array: the largest
+        // tiles, with a workspace laid out for them alone (the array serves
+        // only this entry point)
+        make_plan(*s, &p, 0, false, false);
+        if (p.ws_bytes > kScratchBytes) return UBEP_ERR_UNSUPPORTED;
+    }
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return UBEP_ERR_HIP;
     void* ws = nullptr;

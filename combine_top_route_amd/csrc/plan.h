@@ -113,7 +113,9 @@ struct Plan {
 
 // Host: fill `p` for a shape that passed validation; order 0 (rank order)
 // or 1 (expert order); spread: the tiling with about kTileTarget tiles, else
-// the one with the largest tiles.  The workspace layout depends on neither.
-void make_plan(const ubep_shape& s, Plan* p, int order = 0, bool spread = true);
+// the one with the largest tiles.  The workspace layout depends on neither
+// (it is the spread tiling's) unless ws_spread is false, when it is laid out
+// for the tiling in use alone.
+void make_plan(const ubep_shape& s, Plan* p, int order = 0, bool spread = true, bool ws_spread = true);
 
 }  // namespace ubep

@@ -153,8 +153,10 @@ ubep_status ubep_layout(const ubep_shape *shape /*host*/, const int32_t *topk_id
  * again first (pass it after a call that reported UBEP_ERR_TIMEOUT).
  * status: caller-owned device uint32 that a detected error sets from 0 to its
  * ubep_status code (first error wins, as the workspace status word; the call
- * never clears it).  A shape whose ubep_workspace_bytes exceeds 8 MiB returns
- * UBEP_ERR_UNSUPPORTED before anything is enqueued. */
+ * never clears it).  Where ubep_workspace_bytes exceeds 8 MiB the call takes
+ * the layout's largest tiles, whose workspace is smaller; a shape whose
+ * workspace exceeds 8 MiB even then returns UBEP_ERR_UNSUPPORTED before
+ * anything is enqueued. */
 ubep_status ubep_layout_noalloc(const ubep_shape *shape /*host*/, const int32_t *topk_idx,
                                 int32_t *pos, int32_t *expert_count, int32_t *rank_count,
                                 int32_t *recv_offset, int32_t *send_offset, int32_t *chunk_offset,

@@ -85,6 +85,20 @@ def test_noalloc_layout_reports_errors_and_resets():
     assert_layout_equal(got, oracle.layout(idx, 8, 2, 1), 1)
 
 
+def test_noalloc_layout_falls_back_to_larger_tiles():
+    """A shape whose workspace (laid out for about 128 tiles) exceeds the
+    array, while its largest tiles need less: the call takes those tiles."""
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    w = custom(T=16384, H=8, E=2048, k=8, R=64, C=1, routing="topk", seed=73)
+    s = w.shape
+    assert ubep.ubep_workspace_bytes(s.as_dict()) > 8 << 20
+    say(f"noalloc layout larger tiles {s}")
+    b = alloc_buffers(s.as_dict(), ubep.BF16, topk_idx=w.topk_idx)
+    got = _noalloc(b, status)
+    assert int(status.item()) == ubep.OK
+    assert_layout_equal(got, oracle.layout(w.topk_idx, s.E, s.R, s.C), s.C)
+
+
 def test_noalloc_layout_rejects_shapes_beyond_the_array():
     status = torch.zeros(1, dtype=torch.int32, device="cuda")
     shape = dict(T=1 << 20, H=8, E=256, k=8, R=64, C=16)            # about 24 MiB of workspace
