@@ -146,9 +146,12 @@ GATE_LAYOUT_CASES = [
 ]
 
 
-def _gate_layout_check(z, s, groups, keep, norm, calls=2):
+def _gate_layout_check(z, s, groups, keep, norm, calls=2, interleave=False):
     """ubep_gate_layout against ubep_gate + ubep_layout and the oracle, on
-    consecutive calls (the counts are cleared for the next call)."""
+    consecutive calls (the counts are cleared for the next call).
+    interleave: a plain ubep_layout on the same workspace after each call
+    (it takes other tiles: about 128 where ubep_gate_layout keeps the
+    largest), checked against the oracle too."""
     from gpu_helpers import LAYOUT_KEYS, assert_layout_equal
     sd = s.as_dict() if hasattr(s, "as_dict") else dict(s)
     T, E, k = sd["T"], sd["E"], sd["k"]
@@ -169,6 +172,23 @@ def _gate_layout_check(z, s, groups, keep, norm, calls=2):
         np.testing.assert_array_equal(to_np(b.topk_idx), oi)
         assert _ulps(to_np(b.topk_w), ow).max() <= WEIGHT_ULPS
         assert_layout_equal({key: to_np(getattr(b, key)) for key in LAYOUT_KEYS}, L, sd["C"])
+        if interleave:
+            for key in LAYOUT_KEYS:
+                getattr(b, key).fill_(-7)
+            ubep.ubep_layout(dict(sd, H=8), b.topk_idx, b.pos, b.expert_count, b.rank_count,
+                             b.recv_offset, b.send_offset, b.chunk_offset if sd["C"] > 1 else None,
+                             b.recv_src, b.ws)
+            torch.cuda.synchronize()
+            assert device_status(b) == ubep.OK, call
+            assert_layout_equal({key: to_np(getattr(b, key)) for key in LAYOUT_KEYS}, L, sd["C"])
+
+
+def test_gate_layout_and_layout_share_a_workspace():
+    """The decode shape: ubep_gate_layout (32 tiles of 1024 rows) and
+    ubep_layout (128 tiles of 256 rows) alternating on one workspace."""
+    r = CONFIGS["dsv3_decode_T4096_H7168_E256_k8_R32"]
+    say("gate_layout and layout alternating")
+    _gate_layout_check(router_logits(r), r.shape, 1, 1, r.weights, calls=3, interleave=True)
 
 
 @pytest.mark.parametrize("name,groups,keep", GATE_LAYOUT_CASES, ids=[c[0] for c in GATE_LAYOUT_CASES])
