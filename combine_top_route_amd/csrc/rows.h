@@ -83,6 +83,11 @@ __device__ __forceinline__ void store16_device(__amdgpu_buffer_rsrc_t r, int64_t
     __builtin_amdgcn_raw_buffer_store_b128(x, r, (int)(v * 16), 0, kCachePolicyDevice);
 }
 
+// The same with the non-temporal hint as well (rows nothing reads soon).
+__device__ __forceinline__ void store16_device_nt(__amdgpu_buffer_rsrc_t r, int64_t v, u32x4 x) {
+    __builtin_amdgcn_raw_buffer_store_b128(x, r, (int)(v * 16), 0, kCachePolicyDevice | kCachePolicyNt);
+}
+
 // The loads also carry the non-temporal hint (the rows are read once): on
 // the 4096-token decode step the chunk pipeline took 399 against 427 us with
 // it and the sentinel pipeline 215 against 261 us; at the 65536-token prefill
@@ -136,6 +141,7 @@ constexpr int64_t kNtTailBytes = 160ll << 20;
 constexpr int64_t kNtxMaxBytes = 2ll << 30;
 
 // recv[pos[t][j]] = x[t] for j = 0..k-1 (bf16 bit copy, no relay buffer).
+// NT: non-temporal stores (device-coherent ones too with COH).
 // COH: write the rows with device-coherent stores (see above).  SKIP0: leave
 // each row's first 16-byte unit unwritten (the caller stores it last).  NTX:
 // read x with non-temporal loads.
@@ -167,7 +173,10 @@ __device__ __forceinline__ void dispatch_row_bf16(const u32x4* __restrict__ x,
 #pragma unroll
                 for (int i = 0; i < VPT; ++i) {
                     const int64_t v = v0 + gtid + (int64_t)i * G;
-                    if (v < nvec && !(SKIP0 && v == 0)) store16_device(rs, v, buf[i]);
+                    if (v < nvec && !(SKIP0 && v == 0)) {
+                        if constexpr (NT) store16_device_nt(rs, v, buf[i]);
+                        else store16_device(rs, v, buf[i]);
+                    }
                 }
             } else {
 #pragma unroll
